@@ -1,0 +1,130 @@
+/*
+ * based.h - C ABI of the MI355X (gfx950) causal Based forward.
+ *
+ * The operation is the one defined on the page "Write a fast Based (Taylor linear attention) forward
+ * kernel" (KBench task spec based_forward.py), fields spec_md and contract_md: for every batch b, head h
+ * and position i,
+ *
+ *     s[i,j] = scale * (q_i . k_j)
+ *     A[i,j] = 1 + s[i,j] + s[i,j]^2 / 2        for j <= i (causal, diagonal included), else 0
+ *     o_i    = ( sum_j A[i,j] v_j ) / ( sum_j A[i,j] + 1e-6 )
+ *
+ * evaluated as linear attention over the feature map phi(x) = [1, x, x(x)x / sqrt(2)] with an fp32 state,
+ * chunked along the sequence (the page allows any chunking or algebraic rearrangement that matches).
+ *
+ * Layouts (all row-major, contiguous, no padding; element (b,t,h,c) of a (B,T,H,X) tensor sits at
+ * ((b*T + t)*H + h)*X + c):
+ *     q, k : (B, T, H, K) bfloat16, device memory, read-only
+ *     v    : (B, T, H, V) bfloat16, device memory, read-only
+ *     out  : (B, T, H, V) bfloat16 or float32, device memory, every element written exactly once
+ *
+ * Supported: K in {8, 16}; V a multiple of 64 in [64, 512]; any B, T, H >= 1 (T need not be a multiple
+ * of any chunk length). Device pointers must be 16-byte aligned; out must not overlap q, k, v or the
+ * workspace.
+ *
+ * Ownership: the caller owns q, k, v, out and any workspace; the library never frees or keeps them.
+ * Execution: asynchronous on `stream` (no device synchronisation); launch errors are returned as
+ * BASED_ERR_HIP, faults inside a kernel surface at the caller's next synchronisation. Argument errors
+ * are detected on the host before any HIP call is made, and nothing is enqueued in that case.
+ * Thread safety: all entry points are re-entrant; the only shared state is a lock-protected per-device
+ * property cache. Calls that share a workspace buffer must be ordered on one stream.
+ * Determinism: for a given device and shape, the reduction order is fixed, so results are bitwise
+ * repeatable.
+ */
+#ifndef BASED_H
+#define BASED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BASED_ABI_VERSION 1
+
+typedef enum {
+    BASED_OK = 0,
+    BASED_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, misalignment, overlap, inf scale */
+    BASED_ERR_UNSUPPORTED = 2,        /* K or V outside the supported set */
+    BASED_ERR_HIP = 3,                /* a HIP runtime call or kernel launch failed */
+    BASED_ERR_OUT_OF_MEMORY = 4,      /* the workspace could not be allocated */
+    BASED_ERR_WORKSPACE_TOO_SMALL = 5 /* the caller's workspace is smaller than required */
+} based_status_t;
+
+typedef enum { BASED_BF16 = 0, BASED_F32 = 1 } based_dtype_t;
+
+/* Returns BASED_ABI_VERSION of the built library. */
+int based_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* based_status_string(based_status_t status);
+
+/* Detail text of the last error returned on the calling thread ("" if none). Valid until the next call
+ * on the same thread. */
+const char* based_last_error_detail(void);
+
+/* Bytes of device workspace `based_forward_ws` needs for this shape (0 if the sequence is processed in a
+ * single segment). The sizes are validated as in based_forward; unsupported shapes return 0. */
+size_t based_forward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V);
+
+/*
+ * Causal Based forward (spec_md / contract_md of the page above).
+ *   scale : query scale, multiplies q only, before the dot product. NaN means "None" on the page, i.e.
+ *           (float)K**-0.5 (the feature dimension K, not V). +-inf is rejected.
+ *   out_dtype : BASED_BF16 (round to nearest even) or BASED_F32.
+ * Gets its workspace with hipMallocAsync / hipFreeAsync on `stream` (stream-ordered).
+ */
+based_status_t based_forward(const void* q, const void* k, const void* v,
+                             int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                             float scale, void* out, based_dtype_t out_dtype, hipStream_t stream);
+
+/* Same as based_forward, with a caller-provided device workspace of at least
+ * based_forward_workspace_bytes(...) bytes (may be NULL when that is 0). No allocation is made. */
+based_status_t based_forward_ws(const void* q, const void* k, const void* v,
+                                int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                float scale, void* out, based_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * Execution plan and instrumentation (same operation; for tests and measurement).
+ * ------------------------------------------------------------------------------------------------- */
+
+/* The sequence is split into `segments` pieces of `segment_len` tokens (the last may be shorter); each
+ * piece of each (b, h, 64-column slice of V) is processed by one wavefront, and the states of earlier
+ * pieces are combined with a prefix sum. Reports the plan chosen for a shape; segment_len_override > 0
+ * forces that length (rounded up to the chunk length of 32). */
+based_status_t based_forward_plan(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                  int64_t segment_len_override, int64_t* segments,
+                                  int64_t* segment_len, size_t* workspace_bytes);
+
+/* Opaque recorder of HIP events placed around every kernel launched by based_forward_ex. */
+typedef struct based_timer based_timer;
+
+/* Creates a recorder with room for `max_launches` kernel launches. */
+based_status_t based_timer_create(int max_launches, based_timer** timer);
+void based_timer_destroy(based_timer* timer);
+/* Forgets all recorded launches (events are reused). */
+void based_timer_reset(based_timer* timer);
+/* Waits for the recorded events and returns, for kernel `kernel_id` (0 = segment state sums,
+ * 1 = segment prefix scan, 2 = chunked read-out), the number of recorded launches and their summed
+ * duration in milliseconds. */
+based_status_t based_timer_read(based_timer* timer, int kernel_id, int* launches, double* total_ms);
+/* Static name of kernel `kernel_id` as it appears in profiler traces, or NULL. */
+const char* based_kernel_name(int kernel_id);
+
+/* based_forward_ws with an optional forced segment length (0 = automatic) and an optional timer
+ * (NULL = none). */
+based_status_t based_forward_ex(const void* q, const void* k, const void* v,
+                                int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                float scale, void* out, based_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes,
+                                int64_t segment_len_override, based_timer* timer, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASED_H */

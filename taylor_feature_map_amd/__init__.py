@@ -1,0 +1,5 @@
+"""MI355X-native causal Based forward (2nd-order Taylor linear attention) on hand-written HIP kernels.
+
+The compute path lives in libbased.so (include/based.h); this package is its thin Python binding.
+"""
+from .based import Timer, based_forward, plan, workspace_bytes  # noqa: F401

@@ -1,0 +1,285 @@
+// C ABI of the causal Based forward: argument validation, execution plan, workspace, launches, timing.
+// The operation and the argument contract follow the page "Write a fast Based (Taylor linear attention)
+// forward kernel", fields spec_md and contract_md (see include/based.h for the full contract).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "based.h"
+#include "based_internal.h"
+
+using based::Plan;
+using based::Shape;
+
+namespace {
+
+thread_local std::string g_detail;
+
+based_status_t fail(based_status_t s, const std::string& msg) {
+  g_detail = msg;
+  return s;
+}
+
+based_status_t ok() {
+  g_detail.clear();
+  return BASED_OK;
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;  // keeps every byte offset far from int64 overflow
+constexpr int64_t kTargetWaves = 1024;           // 256 CUs x 4 SIMDs: one wavefront per SIMD
+constexpr int64_t kMinSegment = 256;             // shorter segments cost more in state traffic than they gain
+
+based_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
+  if (B < 1 || T < 1 || H < 1)
+    return fail(BASED_ERR_INVALID_ARGUMENT, "B, T and H must be >= 1");
+  if (K != 8 && K != 16) return fail(BASED_ERR_UNSUPPORTED, "K must be 8 or 16");
+  if (V < 64 || V > 512 || V % 64 != 0) return fail(BASED_ERR_UNSUPPORTED, "V must be a multiple of 64 in [64, 512]");
+  if (B > kMaxElems / T || B * T > kMaxElems / H || B * T * H > kMaxElems / V)
+    return fail(BASED_ERR_INVALID_ARGUMENT, "tensor too large");
+  return BASED_OK;
+}
+
+Plan make_plan(const Shape& sh, int64_t seg_override) {
+  Plan pl;
+  pl.nvs = sh.V / based::kVSlice;
+  const int64_t ck = based::kChunk;
+  const int64_t t_round = (sh.T + ck - 1) / ck * ck;
+  int64_t L;
+  if (seg_override > 0) {
+    L = (seg_override + ck - 1) / ck * ck;
+  } else {
+    const int64_t items = sh.B * sh.H * pl.nvs;
+    const int64_t g_target = (kTargetWaves + items - 1) / items;
+    L = (sh.T + g_target - 1) / g_target;
+    L = (L + ck - 1) / ck * ck;
+    if (L < kMinSegment) L = kMinSegment;
+  }
+  if (L > t_round) L = t_round;
+  pl.seg_len = L;
+  pl.segments = (sh.T + L - 1) / L;
+  pl.slot_floats = based::state_slot_floats(sh.K);
+  return pl;
+}
+
+size_t workspace_bytes(const Shape& sh, const Plan& pl) {
+  if (pl.segments <= 1) return 0;
+  return static_cast<size_t>(sh.B * sh.H * pl.nvs * (pl.segments - 1) * pl.slot_floats) * sizeof(float);
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct based_timer {
+  std::vector<hipEvent_t> events;  // two per launch
+  std::vector<int> kernel_ids;
+  int capacity = 0;
+  int used = 0;
+};
+
+namespace {
+
+based_status_t run(const void* q, const void* k, const void* v, const Shape& sh, float scale, void* out,
+                   based_dtype_t out_dtype, void* ws, size_t ws_bytes, int64_t seg_override, based_timer* timer,
+                   hipStream_t stream, bool allocate) {
+  if (based_status_t s = check_shape(sh.B, sh.T, sh.H, sh.K, sh.V)) return s;
+  if (!q || !k || !v || !out) return fail(BASED_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if (out_dtype != BASED_BF16 && out_dtype != BASED_F32)
+    return fail(BASED_ERR_INVALID_ARGUMENT, "out_dtype must be BASED_BF16 or BASED_F32");
+  if (std::isinf(scale)) return fail(BASED_ERR_INVALID_ARGUMENT, "scale must be finite (NaN selects K**-0.5)");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(BASED_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  if (seg_override < 0) return fail(BASED_ERR_INVALID_ARGUMENT, "segment length override must be >= 0");
+  if (timer && timer->used + 3 > timer->capacity)
+    return fail(BASED_ERR_INVALID_ARGUMENT, "timer is full; reset it or create a larger one");
+
+  const size_t qk_bytes = static_cast<size_t>(sh.B * sh.T * sh.H * sh.K) * 2;
+  const size_t v_bytes = static_cast<size_t>(sh.B * sh.T * sh.H * sh.V) * 2;
+  const size_t o_bytes = static_cast<size_t>(sh.B * sh.T * sh.H * sh.V) * (out_dtype == BASED_F32 ? 4 : 2);
+  if (overlaps(out, o_bytes, q, qk_bytes) || overlaps(out, o_bytes, k, qk_bytes) ||
+      overlaps(out, o_bytes, v, v_bytes))
+    return fail(BASED_ERR_INVALID_ARGUMENT, "out overlaps an input");
+
+  const Plan pl = make_plan(sh, seg_override);
+  const size_t need = workspace_bytes(sh, pl);
+  if (!allocate) {
+    if (need > 0 && !ws) return fail(BASED_ERR_WORKSPACE_TOO_SMALL, "workspace required but NULL");
+    if (ws_bytes < need)
+      return fail(BASED_ERR_WORKSPACE_TOO_SMALL,
+                  "workspace has " + std::to_string(ws_bytes) + " bytes, needs " + std::to_string(need));
+    if (need > 0 && !aligned16(ws)) return fail(BASED_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    if (overlaps(out, o_bytes, ws, need) || overlaps(ws, need, q, qk_bytes) || overlaps(ws, need, k, qk_bytes) ||
+        overlaps(ws, need, v, v_bytes))
+      return fail(BASED_ERR_INVALID_ARGUMENT, "workspace overlaps a tensor");
+  }
+
+  const float sigma = std::isnan(scale) ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(sh.K))) : scale;
+  const bool out_f32 = out_dtype == BASED_F32;
+
+  float* wsf = static_cast<float*>(ws);
+  if (allocate && need > 0) {
+    void* p = nullptr;
+    const hipError_t e = hipMallocAsync(&p, need, stream);
+    if (e != hipSuccess) return fail(BASED_ERR_OUT_OF_MEMORY, std::string("hipMallocAsync: ") + hipGetErrorString(e));
+    wsf = static_cast<float*>(p);
+  }
+
+  auto launch = [&](int id) -> hipError_t {
+    if (timer) {
+      hipError_t e = hipEventRecord(timer->events[2 * timer->used], stream);
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = based::launch_kernel(id, q, k, v, sh, pl, sigma, wsf, out, out_f32, stream);
+    if (e != hipSuccess) return e;
+    if (timer) {
+      e = hipEventRecord(timer->events[2 * timer->used + 1], stream);
+      if (e != hipSuccess) return e;
+      timer->kernel_ids[timer->used] = id;
+      timer->used += 1;
+    }
+    return hipSuccess;
+  };
+
+  hipError_t e = hipSuccess;
+  if (pl.segments > 1) {
+    e = launch(0);
+    if (e == hipSuccess && pl.segments > 2) e = launch(1);
+  }
+  if (e == hipSuccess) e = launch(2);
+  if (allocate && need > 0) {
+    const hipError_t f = hipFreeAsync(wsf, stream);
+    if (e == hipSuccess) e = f;
+  }
+  if (e != hipSuccess) return fail(BASED_ERR_HIP, std::string("HIP: ") + hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int based_abi_version(void) { return BASED_ABI_VERSION; }
+
+const char* based_status_string(based_status_t status) {
+  switch (status) {
+    case BASED_OK: return "ok";
+    case BASED_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case BASED_ERR_UNSUPPORTED: return "unsupported shape";
+    case BASED_ERR_HIP: return "HIP error";
+    case BASED_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case BASED_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* based_last_error_detail(void) { return g_detail.c_str(); }
+
+size_t based_forward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
+  if (check_shape(B, T, H, K, V) != BASED_OK) return 0;
+  const Shape sh{B, T, H, K, V};
+  return workspace_bytes(sh, make_plan(sh, 0));
+}
+
+based_status_t based_forward_plan(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                  int64_t segment_len_override, int64_t* segments, int64_t* segment_len,
+                                  size_t* ws_bytes) {
+  if (based_status_t s = check_shape(B, T, H, K, V)) return s;
+  if (segment_len_override < 0) return fail(BASED_ERR_INVALID_ARGUMENT, "segment length override must be >= 0");
+  const Shape sh{B, T, H, K, V};
+  const Plan pl = make_plan(sh, segment_len_override);
+  if (segments) *segments = pl.segments;
+  if (segment_len) *segment_len = pl.seg_len;
+  if (ws_bytes) *ws_bytes = workspace_bytes(sh, pl);
+  return ok();
+}
+
+based_status_t based_forward(const void* q, const void* k, const void* v, int64_t B, int64_t T, int64_t H,
+                             int64_t K, int64_t V, float scale, void* out, based_dtype_t out_dtype,
+                             hipStream_t stream) {
+  return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, nullptr, 0, 0, nullptr, stream, true);
+}
+
+based_status_t based_forward_ws(const void* q, const void* k, const void* v, int64_t B, int64_t T, int64_t H,
+                                int64_t K, int64_t V, float scale, void* out, based_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, workspace, workspace_bytes, 0, nullptr, stream,
+             false);
+}
+
+based_status_t based_forward_ex(const void* q, const void* k, const void* v, int64_t B, int64_t T, int64_t H,
+                                int64_t K, int64_t V, float scale, void* out, based_dtype_t out_dtype,
+                                void* workspace, size_t workspace_bytes, int64_t segment_len_override,
+                                based_timer* timer, hipStream_t stream) {
+  return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, workspace, workspace_bytes, segment_len_override,
+             timer, stream, false);
+}
+
+based_status_t based_timer_create(int max_launches, based_timer** timer) {
+  if (!timer || max_launches < 1 || max_launches > (1 << 20))
+    return fail(BASED_ERR_INVALID_ARGUMENT, "timer: bad arguments");
+  *timer = nullptr;
+  based_timer* t = new based_timer;
+  t->capacity = max_launches;
+  t->events.assign(2 * static_cast<size_t>(max_launches), nullptr);
+  t->kernel_ids.assign(static_cast<size_t>(max_launches), -1);
+  for (auto& ev : t->events) {
+    const hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) {
+      based_timer_destroy(t);
+      return fail(BASED_ERR_HIP, std::string("hipEventCreate: ") + hipGetErrorString(e));
+    }
+  }
+  *timer = t;
+  return ok();
+}
+
+void based_timer_destroy(based_timer* timer) {
+  if (!timer) return;
+  for (auto& ev : timer->events)
+    if (ev) (void)hipEventDestroy(ev);
+  delete timer;
+}
+
+void based_timer_reset(based_timer* timer) {
+  if (timer) timer->used = 0;
+}
+
+based_status_t based_timer_read(based_timer* timer, int kernel_id, int* launches, double* total_ms) {
+  if (!timer || !launches || !total_ms) return fail(BASED_ERR_INVALID_ARGUMENT, "timer: bad arguments");
+  int n = 0;
+  double sum = 0.0;
+  for (int i = 0; i < timer->used; ++i) {
+    if (timer->kernel_ids[i] != kernel_id) continue;
+    hipError_t e = hipEventSynchronize(timer->events[2 * i + 1]);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, timer->events[2 * i], timer->events[2 * i + 1]);
+    if (e != hipSuccess) return fail(BASED_ERR_HIP, std::string("timer: ") + hipGetErrorString(e));
+    ++n;
+    sum += ms;
+  }
+  *launches = n;
+  *total_ms = sum;
+  return ok();
+}
+
+const char* based_kernel_name(int kernel_id) {
+  switch (kernel_id) {
+    case 0: return "based_segment_state_kernel";
+    case 1: return "based_segment_scan_kernel";
+    case 2: return "based_chunk_readout_kernel";
+  }
+  return nullptr;
+}
+
+}  // extern "C"

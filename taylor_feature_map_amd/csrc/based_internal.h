@@ -1,0 +1,40 @@
+// Internal declarations shared by the kernels and the C-ABI layer of the causal Based forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace based {
+
+constexpr int kWave = 64;    // wavefront width on CDNA
+constexpr int kChunk = 32;   // tokens per chunk (one 16x16x32 MFMA contraction step)
+constexpr int kVSlice = 64;  // value columns per wavefront
+constexpr int kVT = 5;       // 16-column value tiles per wavefront: 4 of values, 1 of ones
+
+struct Shape {
+  int64_t B, T, H, K, V;
+};
+
+// Sequence split: `segments` pieces of `seg_len` tokens (last one possibly shorter), `nvs` value
+// slices of 64 columns, `slot_floats` floats per stored segment state.
+struct Plan {
+  int64_t segments, seg_len, nvs, slot_floats;
+};
+
+template <int B, int E, typename F>
+__host__ __device__ __forceinline__ void constexpr_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    constexpr_for<B + 1, E>(f);
+  }
+}
+
+int state_slot_floats(int64_t K);
+
+// kernel_id: 0 = segment state sums, 1 = prefix over segments, 2 = chunked read-out.
+hipError_t launch_kernel(int kernel_id, const void* q, const void* k, const void* v, const Shape& sh,
+                         const Plan& pl, float sigma, float* ws, void* out, bool out_f32, hipStream_t stream);
+
+}  // namespace based

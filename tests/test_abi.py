@@ -1,0 +1,87 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol include/based.h declares, and rejects
+bad arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from taylor_feature_map_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "based.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(based_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    syms = header_symbols()
+    assert syms, "no declarations found"
+    assert sorted(_lib.SIGNATURES) == syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in header_symbols():
+        assert hasattr(lib, name), name
+    assert lib.based_abi_version() == 1
+    for s in range(6):
+        assert lib.based_status_string(s)
+    assert lib.based_kernel_name(2) == b"based_chunk_readout_kernel"
+    assert lib.based_kernel_name(7) is None
+
+
+FAKE = 0x10000  # aligned non-null address; validation rejects the call before it is ever dereferenced
+
+
+def call(q=FAKE, k=FAKE, v=FAKE, B=1, T=64, H=2, K=16, V=64, scale=math.nan, out=0x80000000, dt=0):
+    lib = _lib.lib()
+    return lib.based_forward(q, k, v, B, T, H, K, V, scale, out, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(out=0), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(B=0), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(T=0), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(H=-1), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(K=12), _lib.BASED_ERR_UNSUPPORTED),
+    (dict(V=96), _lib.BASED_ERR_UNSUPPORTED),
+    (dict(V=1024), _lib.BASED_ERR_UNSUPPORTED),
+    (dict(scale=math.inf), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(scale=-math.inf), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 2), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(dt=7), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(out=FAKE), _lib.BASED_ERR_INVALID_ARGUMENT),  # out overlaps the inputs
+])
+def test_invalid_arguments_rejected_on_host(kw, status):
+    assert call(**kw) == status
+    assert _lib.lib().based_last_error_detail()
+
+
+def test_workspace_checks():
+    lib = _lib.lib()
+    need = lib.based_forward_workspace_bytes(4, 8192, 16, 16, 64)
+    assert need > 0
+    st = lib.based_forward_ws(FAKE, FAKE, FAKE, 4, 8192, 16, 16, 64, math.nan, 0x8000000000, 0, None, 0, None)
+    assert st == _lib.BASED_ERR_WORKSPACE_TOO_SMALL
+    st = lib.based_forward_ws(FAKE, FAKE, FAKE, 4, 8192, 16, 16, 64, math.nan, 0x8000000000, 0, 0x100000000,
+                              need - 1, None)
+    assert st == _lib.BASED_ERR_WORKSPACE_TOO_SMALL
+    assert lib.based_forward_workspace_bytes(1, 64, 1, 12, 64) == 0
+
+
+def test_plan():
+    from taylor_feature_map_amd import plan
+    g, L, ws = plan(4, 8192, 16, 16, 64)
+    assert L % 32 == 0 and g == -(-8192 // L) and g * 64 >= 1024
+    g, L, ws = plan(1, 65000, 16, 16, 64)
+    assert (g - 1) * L < 65000 <= g * L
+    g, L, ws = plan(1, 100, 1, 8, 64, segment_len=1000)
+    assert g == 1 and ws == 0
+    g, L, ws = plan(1, 100, 1, 8, 64, segment_len=33)
+    assert L == 64 and g == 2
