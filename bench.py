@@ -1,0 +1,243 @@
+"""Benchmark of the causal Based forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|INDEX] [--no-cpu-baseline] [--all]
+
+A step is one full forward (every kernel of the path) over one batch of synthetic bf16 inputs that are
+resident in device memory before timing starts. The default workload is B=4, T=8192, H=16, K=16, V=64 with
+bf16 output. Prints one JSON line on stdout; diagnostics go to stderr.
+
+Work model: canonical FLOPs B*H*T*(4*P*V + 2*64*(K+V)), P = 1+K+K*K (field flops_src of the page "Write a
+fast Based (Taylor linear attention) forward kernel"); algorithmic bytes = q, k, v read once + o written
+once = B*T*H*(4K + 2V) + B*T*H*V*(2 or 4).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Based fwd tokens/s and TFLOP/s (% of MFMA/HBM roofline), B=4 T=8192 H=16 K=16"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def canonical_flops(B, T, H, K, V, C=64):
+    P = 1 + K + K * K
+    return B * H * T * (4 * P * V + 2 * C * (K + V))
+
+
+def algorithmic_bytes(B, T, H, K, V, out_bytes):
+    return B * T * H * (4 * K + 2 * V) + B * T * H * V * out_bytes
+
+
+def pick_workload(sel):
+    from taylor_feature_map_amd.inputs import HEADLINE, WORKLOADS
+    if sel is None:
+        return HEADLINE
+    if sel.isdigit():
+        return WORKLOADS[int(sel)]
+    for w in WORKLOADS:
+        if w.name == sel:
+            return w
+    raise SystemExit(f"unknown workload {sel}; choose from {[w.name for w in WORKLOADS]}")
+
+
+def cpu_baseline(w, qb, kb, vb, budget_s=15.0):
+    """The oracle's chunked feature-map form (float64 numpy, chunk 256) on whole (b, h) sequences of the
+    same workload, as many (b, h) pairs as fit in about `budget_s` seconds; scaled to tokens/s of the
+    whole workload."""
+    from oracle import based_ref_chunked, bf16_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done, t_total = 0, 0.0
+    for b, h in pairs:
+        q = bf16_to_f64(qb[b:b + 1, :, h:h + 1])
+        k = bf16_to_f64(kb[b:b + 1, :, h:h + 1])
+        v = bf16_to_f64(vb[b:b + 1, :, h:h + 1])
+        t0 = time.perf_counter()
+        based_ref_chunked(q, k, v, w.scale, 256)
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total >= budget_s:
+            break
+    tokens_equiv = w.B * w.T * done / len(pairs)
+    return {
+        "value": tokens_equiv / t_total,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {len(pairs)} (b,h) sequences of T={w.T} through the float64 chunked oracle "
+                  f"(chunk 256) in {t_total:.2f} s; tokens/s scaled to the whole B*T workload",
+        "seconds": round(t_total, 3),
+        "canonical_gflops": canonical_flops(1, w.T, done, w.K, w.V) / t_total / 1e9,
+    }
+
+
+def run_bench(w, steps, warmup, with_cpu=True):
+    import torch
+
+    from taylor_feature_map_amd import Timer, based_forward, plan
+    from taylor_feature_map_amd.inputs import make_workload
+
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    qb, kb, vb = make_workload(w)
+    to = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to(qb), to(kb), to(vb)
+    out_dtype = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
+    out = torch.empty((w.B, w.T, w.H, w.V), dtype=out_dtype, device=dev)
+    segments, seg_len, ws_bytes = plan(w.B, w.T, w.H, w.K, w.V)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    timer = Timer(max_launches=3 * (steps + warmup) + 16)
+
+    def step(t=None):
+        based_forward(q, k, v, w.scale, out=out, workspace=ws, timer=t)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K back-to-back steps, HIP events around every kernel launch on the launch stream.
+    timer.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / steps
+    per_kernel = {}
+    for kid in Timer.KERNELS:
+        n, ms = timer.read(kid)
+        if n:
+            per_kernel[Timer.kernel_name(kid)] = {"launches": n, "avg_us": ms * 1e3 / n}
+
+    # Same steps without instrumentation, for reference.
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_plain = (time.perf_counter() - t1) * 1e3 / steps
+
+    # Cold-cache steps: a 512 MiB write between steps evicts L2 and the Infinity Cache.
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(min(steps, 10)):
+        flush.zero_()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+
+    out_bytes = 4 if w.out_dtype == "f32" else 2
+    flops = canonical_flops(w.B, w.T, w.H, w.K, w.V)
+    nbytes = algorithmic_bytes(w.B, w.T, w.H, w.K, w.V, out_bytes)
+    tokens = w.B * w.T
+    dom = "based_chunk_readout_kernel"
+    dom_us = per_kernel[dom]["avg_us"]
+    achieved = nbytes / (dom_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
+                   "scale": w.scale, "out_dtype": w.out_dtype, "seed": w.seed,
+                   "segments": segments, "segment_len": seg_len},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": dom_us},
+        "tflops_canonical": flops / (ms_per_step * 1e-3) / 1e12,
+        "path_hbm_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "ms_per_step_uninstrumented": ms_plain,
+        "ms_per_step_cold_median": float(np.median(cold)) if cold else None,
+        "kernels": per_kernel,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+    }
+    if with_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, qb, kb, vb)
+    return result
+
+
+def copy_probe(mib, reps):
+    """A plain copy of known size: reads and writes mib MiB per launch. Profiler counters taken on it give
+    the factor between counter readings and bytes moved."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib * 1024 * 1024 // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true", help="also print a line per workload to stderr")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (counter calibration)")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this implementation has no multi-GPU path "
+              "(every (batch, head) pair is independent; see the sharding notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if a.copy_probe_mib > 0:
+        copy_probe(a.copy_probe_mib, a.steps)
+        return
+    if a.steps < 1 or a.warmup < 0:
+        raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+    if a.all:
+        from taylor_feature_map_amd.inputs import WORKLOADS
+        for w in WORKLOADS:
+            r = run_bench(w, a.steps, a.warmup, with_cpu=False)
+            log(json.dumps({"workload": w.name, "ms_per_step": r["ms_per_step"],
+                            "cold_ms": r["ms_per_step_cold_median"], "tokens_per_s": r["value"],
+                            "tflops": r["tflops_canonical"], "path_hbm_frac": r["path_hbm_frac"],
+                            "kernels": r["kernels"]}))
+    w = pick_workload(a.workload)
+    res = run_bench(w, a.steps, a.warmup, with_cpu=not a.no_cpu_baseline)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
