@@ -18,6 +18,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-function",
+    # MFMA accumulators in ordinary VGPRs: the state is converted to bf16 by VALU every chunk, which
+    # would otherwise need an accumulator-register read per element.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # Packed fp32 VALU forms are kept out of the device code on purpose.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,

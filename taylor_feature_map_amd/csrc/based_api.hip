@@ -31,7 +31,7 @@ based_status_t ok() {
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;  // keeps every byte offset far from int64 overflow
-constexpr int64_t kTargetWaves = 1024;           // 256 CUs x 4 SIMDs: one wavefront per SIMD
+constexpr int64_t kTargetItems = 1024;           // 256 CUs x 4 SIMDs x 2 resident waves, 2 waves per item
 constexpr int64_t kMinSegment = 256;             // shorter segments cost more in state traffic than they gain
 
 based_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
@@ -54,7 +54,7 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
     L = (seg_override + ck - 1) / ck * ck;
   } else {
     const int64_t items = sh.B * sh.H * pl.nvs;
-    const int64_t g_target = (kTargetWaves + items - 1) / items;
+    const int64_t g_target = (kTargetItems + items - 1) / items;
     L = (sh.T + g_target - 1) / g_target;
     L = (L + ck - 1) / ck * ck;
     if (L < kMinSegment) L = kMinSegment;
