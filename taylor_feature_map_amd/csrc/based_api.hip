@@ -31,8 +31,9 @@ based_status_t ok() {
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;  // keeps every byte offset far from int64 overflow
-constexpr int64_t kTargetItems = 1024;           // 256 CUs x 4 SIMDs x 2 resident waves, 2 waves per item
+constexpr int64_t kTargetWaves = 2048;           // 256 CUs x 4 SIMDs x 2 resident waves
 constexpr int64_t kMinSegment = 256;             // shorter segments cost more in state traffic than they gain
+constexpr int64_t kMaxRowRange = 0x7fffffff;     // bytes addressable through one 32-bit buffer range
 
 based_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
   if (B < 1 || T < 1 || H < 1)
@@ -41,20 +42,23 @@ based_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V
   if (V < 64 || V > 512 || V % 64 != 0) return fail(BASED_ERR_UNSUPPORTED, "V must be a multiple of 64 in [64, 512]");
   if (B > kMaxElems / T || B * T > kMaxElems / H || B * T * H > kMaxElems / V)
     return fail(BASED_ERR_INVALID_ARGUMENT, "tensor too large");
+  // The kernels address the rows of one (b, h) through 32-bit buffer ranges of T * H * V * 4 bytes.
+  if (T * H * V * 4 > kMaxRowRange)
+    return fail(BASED_ERR_UNSUPPORTED, "T * H * V * 4 must not exceed 2^31 - 1 bytes");
   return BASED_OK;
 }
 
 Plan make_plan(const Shape& sh, int64_t seg_override) {
   Plan pl;
   pl.nvs = sh.V / based::kVSlice;
-  const int64_t ck = based::kChunk;
+  const int64_t ck = based::chunk_tokens(sh.K);
   const int64_t t_round = (sh.T + ck - 1) / ck * ck;
   int64_t L;
   if (seg_override > 0) {
     L = (seg_override + ck - 1) / ck * ck;
   } else {
-    const int64_t items = sh.B * sh.H * pl.nvs;
-    const int64_t g_target = (kTargetItems + items - 1) / items;
+    const int64_t waves = sh.B * sh.H * pl.nvs * (ck / 32);
+    const int64_t g_target = (kTargetWaves + waves - 1) / waves;
     L = (sh.T + g_target - 1) / g_target;
     L = (L + ck - 1) / ck * ck;
     if (L < kMinSegment) L = kMinSegment;

@@ -9,7 +9,6 @@
 namespace based {
 
 constexpr int kWave = 64;    // wavefront width on CDNA
-constexpr int kChunk = 32;   // tokens per chunk (one 16x16x32 MFMA contraction step)
 constexpr int kVSlice = 64;  // value columns per wavefront
 constexpr int kVT = 5;       // 16-column value tiles per wavefront: 4 of values, 1 of ones
 
@@ -32,6 +31,10 @@ __host__ __device__ __forceinline__ void constexpr_for(F&& f) {
 }
 
 int state_slot_floats(int64_t K);
+
+// Tokens per chunk for feature dimension K; a work item runs on chunk_tokens(K) / 32 wavefronts and
+// segment lengths are multiples of it.
+int chunk_tokens(int64_t K);
 
 // kernel_id: 0 = segment state sums, 1 = prefix over segments, 2 = chunked read-out.
 hipError_t launch_kernel(int kernel_id, const void* q, const void* k, const void* v, const Shape& sh,

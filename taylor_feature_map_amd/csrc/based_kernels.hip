@@ -57,7 +57,6 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16;
 
 constexpr unsigned kOnesBf16x2 = 0x3F803F80u;
-constexpr int kNW = 2;  // wavefronts per work item
 
 // ------------------------------------------------------------------------------------------ helpers
 
@@ -187,109 +186,157 @@ struct Feat<8> {
   }
 };
 
-// Feature tiles owned by wave W: [T0, T0 + NT). K = 16: 5 + 5; K = 8: 2 + 1.
-template <int K, int W>
-struct Tiles {
-  static constexpr int T0 = (K == 16) ? 5 * W : 2 * W;
-  static constexpr int NT = (K == 16) ? 5 : (W == 0 ? 2 : 1);
-  static constexpr int NKS = (NT + 1) / 2;  // 32-deep contraction steps of the read-out
+// ----------------------------------------------------------------------------- work split
+
+// One work item (b, h, value slice, segment) runs on a workgroup of W waves over chunks of C = 32 W
+// tokens. Wave w owns the state feature tiles [T0(w), T0(w) + NT(w)) for the update, and finishes
+// the 16-token query tiles w and 2W - 1 - w of every chunk (this pairing gives every wave the same
+// causal intra-chunk work). K = 16: W = 4, tiles 3 + 3 + 2 + 2, C = 128; K = 8: W = 2, tiles 2 + 1,
+// C = 64.
+template <int K>
+struct Split {
+  static constexpr int W = (K == 16) ? 4 : 2;
+  static constexpr int C = 32 * W;
+  __host__ __device__ static constexpr int T0(int w) { return (K == 16) ? (w < 2 ? 3 * w : 6 + 2 * (w - 2)) : 2 * w; }
+  __host__ __device__ static constexpr int NT(int w) { return (K == 16) ? (w < 2 ? 3 : 2) : (w == 0 ? 2 : 1); }
 };
 
 // ------------------------------------------------------------------------------ LDS staging
 
-// One 32-token chunk of one (b, h, value slice), natural row layout:
-//   K = 16: q[32][16], k[32][16];  K = 8: q[32][8] then k[32][8] inside `q`.
-//   v: 4 blocks of 8 tokens x 64 columns; within a token row the 16-byte unit `oct` (columns
-//   8 oct .. 8 oct + 7) is stored at position oct ^ (token % 8).
+// One chunk of one (b, h, value slice), natural row layout: q[C][K], k[C][K], and v in blocks of 8
+// tokens x 64 columns where the 16-byte unit `oct` (columns 8 oct .. 8 oct + 7) of token t is stored at
+// position oct ^ (t % 8).
+template <int K>
 struct __align__(16) Stage {
-  u16 q[512];
-  u16 k[512];
-  u16 v[2048];
+  static constexpr int C = Split<K>::C;
+  u16 q[C * K];
+  u16 k[C * K];
+  u16 v[C * 64];
 };
 
 __device__ __forceinline__ int v_index(int tok, int col) {
   return (tok >> 3) * 512 + (tok & 7) * 64 + (((col >> 3) ^ (tok & 7)) << 3) + (col & 7);
 }
 
-// Three 16-byte loads per lane per chunk. Wave W: r[0] = q (W = 0) or k (W = 1) rows for K = 16
-// (K = 8: W = 0 loads q into lanes 0..31 and k into lanes 32..63, W = 1 loads none), r[1], r[2] = value
-// blocks 2W and 2W + 1. Tokens >= T are clamped to T - 1: they only ever meet zero Taylor weights.
-template <int K, int W, bool WITH_Q>
-struct Prefetch {
-  u32x4_t r[3];
-
-  __device__ __forceinline__ void load(const u16* __restrict__ qb, const u16* __restrict__ kb,
-                                       const u16* __restrict__ vb, int64_t t0, int64_t T, int64_t qk_stride,
-                                       int64_t v_stride, int lane) {
-    if constexpr (K == 16) {
-      const u16* src = (W == 0) ? qb : kb;
-      if (W == 1 || WITH_Q) {
-        int64_t t = t0 + (lane >> 1);
-        t = t < T ? t : T - 1;
-        r[0] = *reinterpret_cast<const u32x4_t*>(src + t * qk_stride + (lane & 1) * 8);
-      }
-    } else if constexpr (W == 0) {
-      int64_t t = t0 + (lane & 31);
-      t = t < T ? t : T - 1;
-      const u16* src = (lane < 32) ? qb : kb;
-      if (lane >= 32 || WITH_Q) r[0] = *reinterpret_cast<const u32x4_t*>(src + t * qk_stride);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int blk = 2 * W + j;
-      const int row = lane >> 3;
-      int64_t t = t0 + blk * 8 + row;
-      t = t < T ? t : T - 1;
-      const int oct = (lane & 7) ^ row;
-      r[1 + j] = *reinterpret_cast<const u32x4_t*>(vb + t * v_stride + oct * 8);
-    }
+// The 16-byte units of one chunk: NQK q units, NQK k units, then 8 C value units. Unit u lands at u16
+// offset 8 u of its LDS region. Global reads go through buffer resources whose range ends at token T, so
+// units of tokens >= T read as zero; such tokens only ever meet zero Taylor weights or an update whose
+// result is discarded.
+template <int K>
+struct Units {
+  static constexpr int C = Split<K>::C;
+  static constexpr int NQK = C * K / 8;
+  static constexpr int NV = C * 8;
+  static constexpr int NU = 2 * NQK + NV;
+  static constexpr int PER_Q = K / 8;  // units per token row of q or k
+  // Byte offset of q/k unit u relative to the chunk's first token.
+  __device__ static __forceinline__ unsigned qk_off(int u, unsigned stride_bytes) {
+    return (u / PER_Q) * stride_bytes + (u % PER_Q) * 16;
   }
-
-  __device__ __forceinline__ void store(Stage& st, int lane) const {
-    if constexpr (K == 16) {
-      if (W == 1 || WITH_Q) {
-        u16* dst = (W == 0) ? st.q : st.k;
-        *reinterpret_cast<u32x4_t*>(dst + lane * 8) = r[0];
-      }
-    } else if constexpr (W == 0) {
-      if (lane >= 32 || WITH_Q) *reinterpret_cast<u32x4_t*>(st.q + lane * 8) = r[0];
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4_t*>(st.v + (2 * W + j) * 512 + lane * 8) = r[1 + j];
+  // Byte offset of value unit f relative to the chunk's first token.
+  __device__ static __forceinline__ unsigned v_off(int f, unsigned stride_bytes) {
+    const int blk = f >> 6, l = f & 63, row = l >> 3;
+    return (blk * 8 + row) * stride_bytes + (((l & 7) ^ row) << 4);
   }
 };
 
-// B operand of value tile vt: column m <-> value column 16 vt + m; slot e <-> token 16(e/4) + 4g + e%4.
-__device__ __forceinline__ u32x4_t value_operand(const Stage& st, int vt, int lane) {
+// Buffer resource over the rows of one (b, h, value slice): base points at token 0, the range ends at
+// token T (stride_bytes per token).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t T, int64_t stride_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(T * stride_bytes),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Per-item global addressing: buffer resources and row strides in bytes.
+struct Rows {
+  __amdgpu_buffer_rsrc_t q, k, v;
+  unsigned qk_stride, v_stride;
+};
+
+// Chunk loader: the units of q (if WITH_Q), k and v spread over all threads of the workgroup, one
+// chunk ahead of use, through registers. Every region is a multiple of 64 units long, so the region of
+// each of wave WI's loads is known at compile time (no divergent branches around the loads).
+template <int K, bool WITH_Q, int WI>
+struct Prefetch {
+  using U = Units<K>;
+  static constexpr int NTH = Split<K>::W * kWave;
+  static constexpr int FIRST = WITH_Q ? 0 : U::NQK;  // q units are skipped without q
+  static constexpr int PER = (U::NU - FIRST + NTH - 1) / NTH;
+  static_assert(U::NQK % kWave == 0 && U::NV % kWave == 0, "regions must be whole waves");
+  // First unit of load i of this wave, and its region: 0 = q, 1 = k, 2 = v, 3 = none.
+  static constexpr int u0(int i) { return FIRST + WI * kWave + i * NTH; }
+  static constexpr int region(int i) {
+    return u0(i) >= U::NU ? 3 : u0(i) >= 2 * U::NQK ? 2 : u0(i) >= U::NQK ? 1 : 0;
+  }
+  u32x4_t r[PER];
+  unsigned off[PER];
+  __device__ __forceinline__ void init(const Rows& rw, int lane) {
+    constexpr_for<0, PER>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int reg = region(i);
+      const int u = u0(i) + lane;
+      if constexpr (reg == 0) off[i] = U::qk_off(u, rw.qk_stride);
+      else if constexpr (reg == 1) off[i] = U::qk_off(u - U::NQK, rw.qk_stride);
+      else if constexpr (reg == 2) off[i] = U::v_off(u - 2 * U::NQK, rw.v_stride);
+    });
+  }
+  __device__ __forceinline__ void load(const Rows& rw, int64_t t0) {
+    const unsigned sqk = static_cast<unsigned>(t0) * rw.qk_stride;
+    const unsigned sv = static_cast<unsigned>(t0) * rw.v_stride;
+    constexpr_for<0, PER>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int reg = region(i);
+      if constexpr (reg == 0) r[i] = buf_load16(rw.q, off[i], sqk);
+      else if constexpr (reg == 1) r[i] = buf_load16(rw.k, off[i], sqk);
+      else if constexpr (reg == 2) r[i] = buf_load16(rw.v, off[i], sv);
+    });
+  }
+  __device__ __forceinline__ void store(Stage<K>& st, int lane) const {
+    constexpr_for<0, PER>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int reg = region(i);
+      const int u = u0(i) + lane;
+      if constexpr (reg == 0) *reinterpret_cast<u32x4_t*>(st.q + u * 8) = r[i];
+      else if constexpr (reg == 1) *reinterpret_cast<u32x4_t*>(st.k + (u - U::NQK) * 8) = r[i];
+      else if constexpr (reg == 2) *reinterpret_cast<u32x4_t*>(st.v + (u - 2 * U::NQK) * 8) = r[i];
+    });
+  }
+};
+
+// B operand of value tile vt for contraction step ks (tokens 32 ks .. 32 ks + 31): column m <-> value
+// column 16 vt + m; slot e <-> token 32 ks + 16(e/4) + 4g + e%4.
+template <int K>
+__device__ __forceinline__ u32x4_t value_operand(const Stage<K>& st, int ks, int vt, int lane) {
   const int g = lane >> 4, r = lane & 15;
   const int col = 16 * vt + 4 * (r & 3);
-  const u32x2_t a = lds_tr16(st.v + v_index(4 * g + (r >> 2), col));
-  const u32x2_t b = lds_tr16(st.v + v_index(16 + 4 * g + (r >> 2), col));
+  const int tok = 32 * ks + 4 * g + (r >> 2);
+  const u32x2_t a = lds_tr16(st.v + v_index(tok, col));
+  const u32x2_t b = lds_tr16(st.v + v_index(tok + 16, col));
   return u32x4_t{a.x, a.y, b.x, b.y};
 }
 
-// Key feature c (K = 8: c % 8) of the lane's 8 token slots, as floats.
+// Key feature c (K = 8: c % 8) of the lane's 8 token slots of contraction step ks, as floats.
 template <int K>
-__device__ __forceinline__ void key_column(const Stage& st, int lane, float* kx) {
+__device__ __forceinline__ void key_column(const Stage<K>& st, int ks, int lane, float* kx) {
   const int g = lane >> 4, r = lane & 15;
-  const u16* base = (K == 16) ? st.k : st.q + 256;
   const int f4 = (K == 16) ? 4 * (r & 3) : 4 * (r & 1);
-  const u32x2_t a = lds_tr16(base + (4 * g + (r >> 2)) * K + f4);
-  const u32x2_t b = lds_tr16(base + (16 + 4 * g + (r >> 2)) * K + f4);
+  const int tok = 32 * ks + 4 * g + (r >> 2);
+  const u32x2_t a = lds_tr16(st.k + tok * K + f4);
+  const u32x2_t b = lds_tr16(st.k + (tok + 16) * K + f4);
   kx[0] = lo_f(a.x); kx[1] = hi_f(a.x); kx[2] = lo_f(a.y); kx[3] = hi_f(a.y);
   kx[4] = lo_f(b.x); kx[5] = hi_f(b.x); kx[6] = lo_f(b.y); kx[7] = hi_f(b.y);
 }
 
-// S[own tiles] (features x [64 values | ones]) += phi(K_chunk)^T [V_chunk | 1].
-template <int K, int W, typename SA>
-__device__ __forceinline__ void state_update(SA& S, const Stage& st, const u32x4_t (&vop)[kVT], int lane) {
-  using TL = Tiles<K, W>;
-  const int c = lane & 15;
-  float kx[8];
-  key_column<K>(st, lane, kx);
-  constexpr_for<0, TL::NT>([&](auto lc) {
+// S[tiles T0 .. T0 + NT) (features x [64 values | ones]) += phi(K)^T [V | 1] over one 32-token step.
+template <int K, int T0, int NT, typename SA>
+__device__ __forceinline__ void state_update_step(SA& S, const float* kx, const u32x4_t (&vop)[kVT], int c) {
+  constexpr_for<0, NT>([&](auto lc) {
     constexpr int lt = decltype(lc)::value;
-    constexpr int t = TL::T0 + lt;
+    constexpr int t = T0 + lt;
     u32x4_t a;
     a.x = pack2(Feat<K>::template kval<t>(kx[0], c), Feat<K>::template kval<t>(kx[1], c));
     a.y = pack2(Feat<K>::template kval<t>(kx[2], c), Feat<K>::template kval<t>(kx[3], c));
@@ -298,6 +345,13 @@ __device__ __forceinline__ void state_update(SA& S, const Stage& st, const u32x4
 #pragma unroll
     for (int vt = 0; vt < kVT; ++vt) S[lt][vt] = mfma32(a, vop[vt], S[lt][vt]);
   });
+}
+
+template <int K>
+__device__ __forceinline__ void load_value_operands(const Stage<K>& st, int ks, int lane, u32x4_t (&vop)[kVT]) {
+#pragma unroll
+  for (int vt = 0; vt < 4; ++vt) vop[vt] = value_operand<K>(st, ks, vt, lane);
+  vop[4] = u32x4_t{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 }
 
 // Register-native layout of one segment state in the workspace: [tile][value tile][row r][lane].
@@ -320,67 +374,87 @@ __device__ __forceinline__ ItemCoords decode_item(int64_t item, int64_t H, int64
   return ic;
 }
 
+template <int K>
+__device__ __forceinline__ Rows make_rows(const u16* q, const u16* k, const u16* v, const Shape& sh,
+                                          const ItemCoords& ic) {
+  const int64_t bh_qk = (ic.b * sh.T * sh.H + ic.h) * K;
+  const int64_t bh_v = (ic.b * sh.T * sh.H + ic.h) * sh.V + ic.vs * kVSlice;
+  Rows rw;
+  rw.qk_stride = static_cast<unsigned>(sh.H * K * 2);
+  rw.v_stride = static_cast<unsigned>(sh.H * sh.V * 2);
+  rw.q = make_rsrc(q + bh_qk, sh.T, rw.qk_stride);
+  rw.k = make_rsrc(k + bh_qk, sh.T, rw.qk_stride);
+  rw.v = make_rsrc(v + bh_v, sh.T, rw.v_stride);
+  return rw;
+}
+
 // ------------------------------------------------------------------ kernel 0: segment state sums
 
+template <int K>
 struct __align__(16) StateSmem {
-  Stage stage[2];
+  Stage<K> stage[2];
 };
 
-template <int K, int W>
-__device__ __forceinline__ void segment_state_body(StateSmem& sm, const u16* __restrict__ kb,
-                                                   const u16* __restrict__ vb, const Shape& sh, int64_t t_begin,
-                                                   int64_t t_end, float* __restrict__ dst) {
-  using TL = Tiles<K, W>;
-  const int lane = threadIdx.x & 63;
-  const int64_t qk_stride = sh.H * K, v_stride = sh.H * sh.V;
-  f32x4_t S[TL::NT][kVT];
+template <int K, int WI>
+__device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows& rw, int64_t t_begin, int64_t t_end,
+                                                   float* __restrict__ dst) {
+  using SP = Split<K>;
+  constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int c = lane & 15;
+  f32x4_t S[NT][kVT];
 #pragma unroll
-  for (int t = 0; t < TL::NT; ++t)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int vt = 0; vt < kVT; ++vt) S[t][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  Prefetch<K, W, false> pf;
-  pf.load(nullptr, kb, vb, t_begin, sh.T, qk_stride, v_stride, lane);
+  // As in the read-out: chunk c + 1 is loaded at the top of iteration c and staged at its end.
+  Prefetch<K, false, WI> pf;
+  pf.init(rw, lane);
+  pf.load(rw, t_begin);
+  pf.store(sm.stage[0], lane);
   int it = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk, ++it) {
-    Stage& st = sm.stage[it & 1];
-    pf.store(st, lane);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += SP::C, ++it) {
+    const Stage<K>& st = sm.stage[it & 1];
+    pf.load(rw, t0 + SP::C);
     __syncthreads();
-    if (t0 + kChunk < t_end) pf.load(nullptr, kb, vb, t0 + kChunk, sh.T, qk_stride, v_stride, lane);
-    u32x4_t vop[kVT];
 #pragma unroll
-    for (int vt = 0; vt < 4; ++vt) vop[vt] = value_operand(st, vt, lane);
-    vop[4] = u32x4_t{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
-    state_update<K, W>(S, st, vop, lane);
+    for (int ks = 0; ks < SP::W; ++ks) {
+      u32x4_t vop[kVT];
+      load_value_operands<K>(st, ks, lane, vop);
+      float kx[8];
+      key_column<K>(st, ks, lane, kx);
+      state_update_step<K, T0, NT>(S, kx, vop, c);
+    }
+    pf.store(sm.stage[(it + 1) & 1], lane);  // read in iteration c - 1, finished before this iteration's barrier
   }
 #pragma unroll
-  for (int lt = 0; lt < TL::NT; ++lt)
+  for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
     for (int vt = 0; vt < kVT; ++vt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[state_offset(TL::T0 + lt, vt, r, lane)] = S[lt][vt][r];
+      for (int r = 0; r < 4; ++r) dst[state_offset(T0 + lt, vt, r, lane)] = S[lt][vt][r];
 }
 
 template <int K>
-__global__ __launch_bounds__(kNW * kWave) void based_segment_state_kernel(const u16* __restrict__ k,
-                                                                           const u16* __restrict__ v, Shape sh,
-                                                                           Plan pl, float* __restrict__ ws) {
+__global__ __launch_bounds__(Split<K>::W * kWave) void based_segment_state_kernel(
+    const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float* __restrict__ ws) {
   const int64_t item = item_of_block();
   const int64_t items = sh.B * sh.H * pl.nvs * (pl.segments - 1);
   if (item >= items) return;
   const ItemCoords ic = decode_item(item, sh.H, pl.nvs, pl.segments - 1);
-  __shared__ StateSmem sm;
-  const u16* kb = k + (ic.b * sh.T * sh.H + ic.h) * K;
-  const u16* vb = v + (ic.b * sh.T * sh.H + ic.h) * sh.V + ic.vs * kVSlice;
+  __shared__ StateSmem<K> sm;
+  const Rows rw = make_rows<K>(k, k, v, sh, ic);
   const int64_t t_begin = ic.g * pl.seg_len;
   const int64_t t_end = t_begin + pl.seg_len;  // full segment: only the last one can be short
   const int64_t bhv = (ic.b * sh.H + ic.h) * pl.nvs + ic.vs;
   float* dst = ws + (bhv * (pl.segments - 1) + ic.g) * pl.slot_floats;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w == 0)
-    segment_state_body<K, 0>(sm, kb, vb, sh, t_begin, t_end, dst);
-  else
-    segment_state_body<K, 1>(sm, kb, vb, sh, t_begin, t_end, dst);
+  constexpr_for<0, Split<K>::W>([&](auto wc) {
+    constexpr int WI = decltype(wc)::value;
+    if (w == WI) segment_state_body<K, WI>(sm, rw, t_begin, t_end, dst);
+  });
 }
 
 // ------------------------------------------------------------- kernel 1: prefix over segments
@@ -403,194 +477,223 @@ __global__ __launch_bounds__(256) void based_segment_scan_kernel(float* __restri
 
 // ------------------------------------------------------------------- kernel 2: chunked read-out
 
+constexpr int kMaxPairs = 5;  // tile pairs of the read-out contraction (K = 16)
+
+template <int K>
 struct __align__(16) ReadoutSmem {
-  Stage stage[2];
-  float xch[kNW][kVT * 4][kWave];  // read-out partial of the other wave's 16-token half
+  Stage<K> stage[2];                  // chunk c in stage[c % 2]; chunk c + 1 is staged during chunk c
+  u32x4_t sb[kMaxPairs][kVT][kWave];  // bf16 state: tile pair m, value tile, lane (D register layout)
 };
 
-template <int K, int W, bool OUT_F32>
-__device__ __forceinline__ void readout_body(ReadoutSmem& sm, const u16* __restrict__ qb,
-                                             const u16* __restrict__ kb, const u16* __restrict__ vb,
-                                             const Shape& sh, int64_t t_begin, int64_t t_end, float c1, float c2,
-                                             float sigma, const float* __restrict__ src, void* __restrict__ out,
-                                             int64_t out_base) {
-  using F = Feat<K>;
-  using TL = Tiles<K, W>;
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 15, g = lane >> 4;
-  const int64_t qk_stride = sh.H * K, v_stride = sh.H * sh.V;
-  const int64_t out_stride = sh.H * sh.V;
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+// bf16 copy of this wave's state tiles into the shared tile-pair layout.
+template <int K, int T0, int NT, typename SA>
+__device__ __forceinline__ void publish_state(ReadoutSmem<K>& sm, const SA& S, int lane) {
+#pragma unroll
+  for (int lt = 0; lt < NT; ++lt) {
+    const int t = T0 + lt;
+#pragma unroll
+    for (int vt = 0; vt < kVT; ++vt) {
+      u32x2_t* d = reinterpret_cast<u32x2_t*>(&sm.sb[t >> 1][vt][lane]) + (t & 1);
+      *d = u32x2_t{pack2(S[lt][vt][0], S[lt][vt][1]), pack2(S[lt][vt][2], S[lt][vt][3])};
+    }
+  }
+}
 
-  f32x4_t S[TL::NT][kVT];
+// Intra-chunk contribution of key step ks (key tokens 32 ks .. 32 ks + 31) to 16-token query tile II:
+// scores K Q^T on the 16x16x16 MFMA, Taylor weights, then A [V | 1].
+template <int K, int II>
+__device__ __forceinline__ void intra_step(const Stage<K>& st, int ks, const u32x4_t (&vop)[kVT], f32x4_t (&O)[kVT],
+                                           float c1, float c2, int lane) {
+  if (2 * ks > II) return;
+  const int c = lane & 15, g = lane >> 4;
+  u32x2_t qb = {0u, 0u};
+  if (K == 16 || g < 2) qb = *reinterpret_cast<const u32x2_t*>(st.q + (16 * II + c) * K + 4 * g);
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t d[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int jj = 2 * ks + h;
+    d[h] = zero4;
+    if (jj <= II) {
+      u32x2_t ka = {0u, 0u};
+      if (K == 16 || g < 2) ka = *reinterpret_cast<const u32x2_t*>(st.k + (16 * jj + c) * K + 4 * g);
+      d[h] = mfma16(ka, qb, zero4);
+    }
+  }
+  // A operand: slot e <-> key token 32 ks + 16(e/4) + 4g + e%4, row (query) 16 II + c.
+  float w[8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int jj = 2 * ks + h;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float a = 0.0f;
+      if (jj <= II) {
+        const float sc = d[h][r];
+        a = fmaf(sc, fmaf(sc, c2, c1), 1.0f);
+        if (jj == II) a = (4 * g + r <= c) ? a : 0.0f;
+      }
+      w[4 * h + r] = a;
+    }
+  }
+  const u32x4_t aop = {pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7])};
+#pragma unroll
+  for (int vt = 0; vt < kVT; ++vt) O[vt] = mfma32(aop, vop[vt], O[vt]);
+}
+
+// o = num / (den + 1e-6) for one 16-token query tile; lane holds rows 4g + r, columns 16 vt + c.
+// voff is the lane's byte offset of (row 4g, column c); the row r and column tile vt go into the scalar
+// offset. Rows past the end of the sequence fall outside the output buffer range and are dropped.
+template <bool OUT_F32>
+__device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned voff, unsigned stride_bytes,
+                                           unsigned soff, const f32x4_t (&O)[kVT]) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float inv = __builtin_amdgcn_rcpf(O[4][r] + 1e-6f);
+    const unsigned so = soff + r * stride_bytes;
+    if constexpr (OUT_F32) {
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, O[vt][r] * inv), ro, voff, so + 64 * vt, 0);
+    } else {
+      const unsigned p01 = pack2(O[0][r] * inv, O[1][r] * inv);
+      const unsigned p23 = pack2(O[2][r] * inv, O[3][r] * inv);
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(p01), ro, voff, so, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(p01 >> 16), ro, voff, so + 32, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(p23), ro, voff, so + 64, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(p23 >> 16), ro, voff, so + 96, 0);
+    }
+  }
+}
+
+template <int K, int WI, bool OUT_F32>
+__device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw, __amdgpu_buffer_rsrc_t ro,
+                                             unsigned out_stride, int64_t t_begin, int64_t t_end, float c1,
+                                             float c2, float sigma, const float* __restrict__ src) {
+  using F = Feat<K>;
+  using SP = Split<K>;
+  constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
+  constexpr int I0 = WI, I1 = 2 * SP::W - 1 - WI;  // this wave's query tiles
+  constexpr int NP = (F::NPT + 1) / 2;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  constexpr unsigned kOutBytes = OUT_F32 ? 4 : 2;
+  const unsigned lane_off = (4 * g) * out_stride + c * kOutBytes;
+
+  f32x4_t S[NT][kVT];
   if (src) {
 #pragma unroll
-    for (int lt = 0; lt < TL::NT; ++lt)
+    for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
       for (int vt = 0; vt < kVT; ++vt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) S[lt][vt][r] = src[state_offset(TL::T0 + lt, vt, r, lane)];
+        for (int r = 0; r < 4; ++r) S[lt][vt][r] = src[state_offset(T0 + lt, vt, r, lane)];
   } else {
 #pragma unroll
-    for (int lt = 0; lt < TL::NT; ++lt)
+    for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
       for (int vt = 0; vt < kVT; ++vt) S[lt][vt] = zero4;
   }
+  publish_state<K, T0, NT>(sm, S, lane);
+  if constexpr (F::NPT % 2 == 1 && T0 + NT == F::NPT) {
+    // The last tile pair is half empty: its second half stays zero for the whole kernel.
+#pragma unroll
+    for (int vt = 0; vt < kVT; ++vt)
+      reinterpret_cast<u32x2_t*>(&sm.sb[F::NPT >> 1][vt][lane])[1] = u32x2_t{0u, 0u};
+  }
 
-  Prefetch<K, W, true> pf;
-  pf.load(qb, kb, vb, t_begin, sh.T, qk_stride, v_stride, lane);
+  // Chunk c is read from stage[c % 2]. Chunk c + 1 is loaded into registers at the top of iteration c
+  // and written to stage[(c + 1) % 2] at its end, so the loads have the whole iteration to arrive and
+  // no load result is pending across the loop's back edge (which would make the memory-counter wait
+  // at the top cover this chunk's output stores too). Loads past the segment read the next segment's
+  // (or out-of-range, zero) rows and are never used.
+  Prefetch<K, true, WI> pf;
+  pf.init(rw, lane);
+  pf.load(rw, t_begin);
+  pf.store(sm.stage[0], lane);
   int it = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += kChunk, ++it) {
-    Stage& st = sm.stage[it & 1];
-    pf.store(st, lane);
-    __syncthreads();
-    if (t0 + kChunk < t_end) pf.load(qb, kb, vb, t0 + kChunk, sh.T, qk_stride, v_stride, lane);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += SP::C, ++it) {
+    pf.load(rw, t0 + SP::C);
+    __syncthreads();  // this chunk's inputs and the bf16 state of earlier chunks are in LDS
+    const Stage<K>& st = sm.stage[it & 1];
 
-    u32x4_t vop[kVT];
-#pragma unroll
-    for (int vt = 0; vt < 4; ++vt) vop[vt] = value_operand(st, vt, lane);
-    vop[4] = u32x4_t{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
-
-    // ---- scores s' = K Q^T for this wave's 16-token half (D[j][i], lane: column i = c, rows j = 4g + r),
-    //      then Taylor weights A = 1 + c1 s' + c2 s'^2 (c1 = scale, c2 = scale^2/2), causal, rounded once.
-    //      A operand: slot e <-> token j = 16(e/4) + 4g + e%4, row i = 16 W + c.
-    u32x4_t aop;
-    {
-      const u16* qarr = st.q;
-      const u16* karr = (K == 16) ? st.k : st.q + 256;
-      u32x2_t ka0 = {0u, 0u}, ka1 = {0u, 0u}, qbw = {0u, 0u};
-      if (K == 16 || g < 2) {
-        ka0 = *reinterpret_cast<const u32x2_t*>(karr + c * K + 4 * g);
-        qbw = *reinterpret_cast<const u32x2_t*>(qarr + (16 * W + c) * K + 4 * g);
-        if (W == 1) ka1 = *reinterpret_cast<const u32x2_t*>(karr + (16 + c) * K + 4 * g);
-      }
-      const f32x4_t d0 = mfma16(ka0, qbw, zero4);  // j-tile 0
-      float w0[4], w1[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float a = fmaf(d0[r], fmaf(d0[r], c2, c1), 1.0f);
-        w0[r] = (W == 1 || 4 * g + r <= c) ? a : 0.0f;
-      }
-      if constexpr (W == 1) {
-        const f32x4_t d1 = mfma16(ka1, qbw, zero4);  // j-tile 1 (diagonal tile of the second half)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = fmaf(d1[r], fmaf(d1[r], c2, c1), 1.0f);
-          w1[r] = (4 * g + r <= c) ? a : 0.0f;
-        }
-        aop = u32x4_t{pack2(w0[0], w0[1]), pack2(w0[2], w0[3]), pack2(w1[0], w1[1]), pack2(w1[2], w1[3])};
-      } else {
-        aop = u32x4_t{pack2(w0[0], w0[1]), pack2(w0[2], w0[3]), 0u, 0u};
-      }
-    }
-
-    // ---- read-out of earlier tokens through this wave's half of the state, for both 16-token halves.
+    // ---- read-out of earlier tokens through the state: O = phi(Q) S for this wave's two query tiles.
     f32x4_t O[2][kVT];
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int vt = 0; vt < kVT; ++vt) O[ii][vt] = zero4;
-
-    float ry[2][F::NQ], hy[2][4];
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const u16* qrow = st.q + (16 * ii + c) * K;
-#pragma unroll
-      for (int kk = 0; kk < F::NQ / 4; ++kk) {
-        const int base = 4 * ((g + kk) & (F::NQ / 4 - 1));
-        const u32x2_t w2 = *reinterpret_cast<const u32x2_t*>(qrow + base);
-        ry[ii][4 * kk + 0] = sigma * lo_f(w2.x);
-        ry[ii][4 * kk + 1] = sigma * hi_f(w2.x);
-        ry[ii][4 * kk + 2] = sigma * lo_f(w2.y);
-        ry[ii][4 * kk + 3] = sigma * hi_f(w2.y);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hy[ii][r] = 0.5f * ry[ii][r];
-    }
-
-    constexpr_for<0, TL::NKS>([&](auto mc) {
-      constexpr int m = decltype(mc)::value;
-      constexpr int ta = TL::T0 + 2 * m, tb = TL::T0 + 2 * m + 1;
-      constexpr bool has_b = (2 * m + 1) < TL::NT;
-      u32x4_t pq[2];
+    {
+      float ry[2][F::NQ], hy[2][4];
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
-        pq[ii].x = pack2(F::template qval<ta, 0>(ry[ii], hy[ii], g), F::template qval<ta, 1>(ry[ii], hy[ii], g));
-        pq[ii].y = pack2(F::template qval<ta, 2>(ry[ii], hy[ii], g), F::template qval<ta, 3>(ry[ii], hy[ii], g));
-        if constexpr (has_b) {
-          pq[ii].z = pack2(F::template qval<tb, 0>(ry[ii], hy[ii], g), F::template qval<tb, 1>(ry[ii], hy[ii], g));
-          pq[ii].w = pack2(F::template qval<tb, 2>(ry[ii], hy[ii], g), F::template qval<tb, 3>(ry[ii], hy[ii], g));
-        } else {
-          pq[ii].z = 0u;
-          pq[ii].w = 0u;
+        const u16* qrow = st.q + (16 * (ii == 0 ? I0 : I1) + c) * K;
+#pragma unroll
+        for (int kk = 0; kk < F::NQ / 4; ++kk) {
+          const int base = 4 * ((g + kk) & (F::NQ / 4 - 1));
+          const u32x2_t w2 = *reinterpret_cast<const u32x2_t*>(qrow + base);
+          ry[ii][4 * kk + 0] = sigma * lo_f(w2.x);
+          ry[ii][4 * kk + 1] = sigma * hi_f(w2.x);
+          ry[ii][4 * kk + 2] = sigma * lo_f(w2.y);
+          ry[ii][4 * kk + 3] = sigma * hi_f(w2.y);
         }
-      }
 #pragma unroll
-      for (int vt = 0; vt < kVT; ++vt) {
-        u32x4_t sb;
-        sb.x = pack2(S[2 * m][vt][0], S[2 * m][vt][1]);
-        sb.y = pack2(S[2 * m][vt][2], S[2 * m][vt][3]);
-        if constexpr (has_b) {
-          sb.z = pack2(S[2 * m + 1][vt][0], S[2 * m + 1][vt][1]);
-          sb.w = pack2(S[2 * m + 1][vt][2], S[2 * m + 1][vt][3]);
-        } else {
-          sb.z = 0u;
-          sb.w = 0u;
+        for (int r = 0; r < 4; ++r) hy[ii][r] = 0.5f * ry[ii][r];
+      }
+      constexpr_for<0, NP>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int ta = 2 * m, tb = 2 * m + 1;
+        u32x4_t sb[kVT];
+#pragma unroll
+        for (int vt = 0; vt < kVT; ++vt) sb[vt] = sm.sb[m][vt][lane];
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          u32x4_t pq;
+          pq.x = pack2(F::template qval<ta, 0>(ry[ii], hy[ii], g), F::template qval<ta, 1>(ry[ii], hy[ii], g));
+          pq.y = pack2(F::template qval<ta, 2>(ry[ii], hy[ii], g), F::template qval<ta, 3>(ry[ii], hy[ii], g));
+          pq.z = pack2(F::template qval<tb, 0>(ry[ii], hy[ii], g), F::template qval<tb, 1>(ry[ii], hy[ii], g));
+          pq.w = pack2(F::template qval<tb, 2>(ry[ii], hy[ii], g), F::template qval<tb, 3>(ry[ii], hy[ii], g));
+#pragma unroll
+          for (int vt = 0; vt < kVT; ++vt) O[ii][vt] = mfma32(pq, sb[vt], m == 0 ? zero4 : O[ii][vt]);
         }
-        O[0][vt] = mfma32(pq[0], sb, O[0][vt]);
-        O[1][vt] = mfma32(pq[1], sb, O[1][vt]);
-      }
-    });
-
-    // ---- hand the other half's partial to the other wave; add the intra-chunk term to ours.
-#pragma unroll
-    for (int vt = 0; vt < kVT; ++vt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm.xch[W][vt * 4 + r][lane] = O[1 - W][vt][r];
-#pragma unroll
-    for (int vt = 0; vt < kVT; ++vt) O[W][vt] = mfma32(aop, vop[vt], O[W][vt]);
-    __syncthreads();
-#pragma unroll
-    for (int vt = 0; vt < kVT; ++vt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) O[W][vt][r] += sm.xch[1 - W][vt * 4 + r][lane];
-
-    // ---- o = num / (den + 1e-6); lane holds rows 16 W + 4g + r, columns 16 vt + c.
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t tok = t0 + 16 * W + 4 * g + r;
-      const float inv = __builtin_amdgcn_rcpf(O[W][4][r] + 1e-6f);
-      if (tok < t_end) {
-        const int64_t off = out_base + tok * out_stride + c;
-#pragma unroll
-        for (int vt = 0; vt < 4; ++vt) {
-          const float o = O[W][vt][r] * inv;
-          if constexpr (OUT_F32) {
-            static_cast<float*>(out)[off + 16 * vt] = o;
-          } else {
-            static_cast<__bf16*>(out)[off + 16 * vt] = static_cast<__bf16>(o);
-          }
-        }
-      }
+      });
     }
 
-    // Unconditional: after the last chunk the state is simply not used (tokens past T were clamped to
-    // finite inputs), and a conditional update would make the compiler copy S every iteration.
-    state_update<K, W>(S, st, vop, lane);
+    // ---- per 32-token key step: intra-chunk term (direct polynomial) for both query tiles, then fold
+    //      the step into this wave's state tiles (after the last chunk the result is unused).
+    const unsigned soff_out = static_cast<unsigned>(t0) * out_stride;
+#pragma unroll
+    for (int ks = 0; ks < SP::W; ++ks) {
+      u32x4_t vop[kVT];
+      load_value_operands<K>(st, ks, lane, vop);
+      intra_step<K, I0>(st, ks, vop, O[0], c1, c2, lane);
+      intra_step<K, I1>(st, ks, vop, O[1], c1, c2, lane);
+      if (ks == SP::W - 1) {
+        store_tile<OUT_F32>(ro, lane_off, out_stride, soff_out + 16 * I0 * out_stride, O[0]);
+        store_tile<OUT_F32>(ro, lane_off, out_stride, soff_out + 16 * I1 * out_stride, O[1]);
+      }
+      float kx[8];
+      key_column<K>(st, ks, lane, kx);
+      state_update_step<K, T0, NT>(S, kx, vop, c);
+    }
+    __syncthreads();  // every wave is done with the old bf16 state
+    publish_state<K, T0, NT>(sm, S, lane);
+    pf.store(sm.stage[(it + 1) & 1], lane);  // that buffer's chunk c - 1 was finished before the last barrier
   }
 }
 
 template <int K, bool OUT_F32>
-__global__ __launch_bounds__(kNW * kWave) void based_chunk_readout_kernel(
+__global__ __launch_bounds__(Split<K>::W * kWave) void based_chunk_readout_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float c1,
     float c2, float sigma, const float* __restrict__ ws, void* __restrict__ out) {
   const int64_t item = item_of_block();
   const int64_t items = sh.B * sh.H * pl.nvs * pl.segments;
   if (item >= items) return;
   const ItemCoords ic = decode_item(item, sh.H, pl.nvs, pl.segments);
-  __shared__ ReadoutSmem sm;
-  const int64_t bh_qk = (ic.b * sh.T * sh.H + ic.h) * K;
+  __shared__ ReadoutSmem<K> sm;
+  const Rows rw = make_rows<K>(q, k, v, sh, ic);
   const int64_t bh_v = (ic.b * sh.T * sh.H + ic.h) * sh.V + ic.vs * kVSlice;
+  const unsigned out_stride = static_cast<unsigned>(sh.H * sh.V * (OUT_F32 ? 4 : 2));
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(static_cast<char*>(out) + bh_v * (OUT_F32 ? 4 : 2), sh.T, out_stride);
   const int64_t t_begin = ic.g * pl.seg_len;
   const int64_t t_end = (t_begin + pl.seg_len < sh.T) ? t_begin + pl.seg_len : sh.T;
   const float* src = nullptr;
@@ -599,12 +702,10 @@ __global__ __launch_bounds__(kNW * kWave) void based_chunk_readout_kernel(
     src = ws + (bhv * (pl.segments - 1) + ic.g - 1) * pl.slot_floats;
   }
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (w == 0)
-    readout_body<K, 0, OUT_F32>(sm, q + bh_qk, k + bh_qk, v + bh_v, sh, t_begin, t_end, c1, c2, sigma, src, out,
-                                bh_v);
-  else
-    readout_body<K, 1, OUT_F32>(sm, q + bh_qk, k + bh_qk, v + bh_v, sh, t_begin, t_end, c1, c2, sigma, src, out,
-                                bh_v);
+  constexpr_for<0, Split<K>::W>([&](auto wc) {
+    constexpr int WI = decltype(wc)::value;
+    if (w == WI) readout_body<K, WI, OUT_F32>(sm, rw, ro, out_stride, t_begin, t_end, c1, c2, sigma, src);
+  });
 }
 
 // ------------------------------------------------------------------------------- host launchers
@@ -614,8 +715,9 @@ hipError_t launch_segment_state(const void* k, const void* v, const Shape& sh, c
                                 hipStream_t stream) {
   const int64_t items = sh.B * sh.H * pl.nvs * (pl.segments - 1);
   const int64_t blocks = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL(based_segment_state_kernel<K>, dim3(static_cast<unsigned>(blocks)), dim3(kNW * kWave), 0,
-                     stream, static_cast<const u16*>(k), static_cast<const u16*>(v), sh, pl, ws);
+  hipLaunchKernelGGL(based_segment_state_kernel<K>, dim3(static_cast<unsigned>(blocks)),
+                     dim3(Split<K>::W * kWave), 0, stream, static_cast<const u16*>(k),
+                     static_cast<const u16*>(v), sh, pl, ws);
   return hipGetLastError();
 }
 
@@ -637,17 +739,19 @@ hipError_t launch_chunk_readout(const void* q, const void* k, const void* v, con
   const float c2 = 0.5f * sigma * sigma;
   if (out_f32) {
     hipLaunchKernelGGL((based_chunk_readout_kernel<K, true>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kNW * kWave), 0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                       dim3(Split<K>::W * kWave), 0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                        static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out);
   } else {
     hipLaunchKernelGGL((based_chunk_readout_kernel<K, false>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kNW * kWave), 0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
+                       dim3(Split<K>::W * kWave), 0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
                        static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out);
   }
   return hipGetLastError();
 }
 
 int state_slot_floats(int64_t K) { return (K == 16 ? Feat<16>::NPT : Feat<8>::NPT) * kVT * 4 * kWave; }
+
+int chunk_tokens(int64_t K) { return K == 16 ? Split<16>::C : Split<8>::C; }
 
 hipError_t launch_kernel(int kernel_id, const void* q, const void* k, const void* v, const Shape& sh,
                          const Plan& pl, float sigma, float* ws, void* out, bool out_f32, hipStream_t stream) {

@@ -65,7 +65,7 @@ def test_parity_full(B, T, H, K, V, scale, out):
 
 
 @pytest.mark.parametrize("K,V", [(16, 64), (8, 128)])
-@pytest.mark.parametrize("seg", [32, 64, 96, 256, 100000])
+@pytest.mark.parametrize("seg", [64, 128, 192, 256, 384, 100000])
 def test_parity_forced_segments(K, V, seg):
     """Every sequence split (several prefix-scan steps, ragged tail, single segment) gives the answer."""
     B, T, H = 1, 777, 2
