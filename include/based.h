@@ -19,15 +19,16 @@
  *     out  : (B, T, H, V) bfloat16 or float32, device memory, every element written exactly once
  *
  * Supported: K in {8, 16}; V a multiple of 64 in [64, 512]; any B, T, H >= 1 (T need not be a multiple
- * of any chunk length). Device pointers must be 16-byte aligned; out must not overlap q, k, v or the
+ * of any chunk length) with T * H * V * 4 <= 2^31 - 1 (the rows of one (b, h) are addressed through
+ * 32-bit buffer ranges). Device pointers must be 16-byte aligned; out must not overlap q, k, v or the
  * workspace.
  *
  * Ownership: the caller owns q, k, v, out and any workspace; the library never frees or keeps them.
  * Execution: asynchronous on `stream` (no device synchronisation); launch errors are returned as
  * BASED_ERR_HIP, faults inside a kernel surface at the caller's next synchronisation. Argument errors
  * are detected on the host before any HIP call is made, and nothing is enqueued in that case.
- * Thread safety: all entry points are re-entrant; the only shared state is a lock-protected per-device
- * property cache. Calls that share a workspace buffer must be ordered on one stream.
+ * Thread safety: all entry points are re-entrant and keep no global state (a timer object must not be
+ * shared between threads). Calls that share a workspace buffer must be ordered on one stream.
  * Determinism: for a given device and shape, the reduction order is fixed, so results are bitwise
  * repeatable.
  */
@@ -48,7 +49,7 @@ extern "C" {
 typedef enum {
     BASED_OK = 0,
     BASED_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, misalignment, overlap, inf scale */
-    BASED_ERR_UNSUPPORTED = 2,        /* K or V outside the supported set */
+    BASED_ERR_UNSUPPORTED = 2,        /* K or V outside the supported set, or T * H * V too large */
     BASED_ERR_HIP = 3,                /* a HIP runtime call or kernel launch failed */
     BASED_ERR_OUT_OF_MEMORY = 4,      /* the workspace could not be allocated */
     BASED_ERR_WORKSPACE_TOO_SMALL = 5 /* the caller's workspace is smaller than required */
@@ -93,14 +94,15 @@ based_status_t based_forward_ws(const void* q, const void* k, const void* v,
  * ------------------------------------------------------------------------------------------------- */
 
 /* The sequence is split into `segments` pieces of `segment_len` tokens (the last may be shorter); each
- * piece of each (b, h, 64-column slice of V) is processed by one wavefront, and the states of earlier
- * pieces are combined with a prefix sum. Reports the plan chosen for a shape; segment_len_override > 0
- * forces that length (rounded up to the chunk length of 32). */
+ * piece of each (b, h, 64-column slice of V) is processed by one workgroup (4 wavefronts for K = 16, 2
+ * for K = 8) in chunks of 128 (K = 16) or 64 (K = 8) tokens, and the states of earlier pieces are
+ * combined with a prefix sum. Reports the plan chosen for a shape; segment_len_override > 0 forces that
+ * length (rounded up to a whole number of chunks). */
 based_status_t based_forward_plan(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                   int64_t segment_len_override, int64_t* segments,
                                   int64_t* segment_len, size_t* workspace_bytes);
 
-/* Opaque recorder of HIP events placed around every kernel launched by based_forward_ex. */
+/* Opaque recorder of HIP events placed around the kernels launched by based_forward_ex. */
 typedef struct based_timer based_timer;
 
 /* Creates a recorder with room for `max_launches` kernel launches. */
@@ -108,6 +110,9 @@ based_status_t based_timer_create(int max_launches, based_timer** timer);
 void based_timer_destroy(based_timer* timer);
 /* Forgets all recorded launches (events are reused). */
 void based_timer_reset(based_timer* timer);
+/* Restricts recording to the kernels whose bit (1 << kernel_id) is set in `mask` (default: all). Each
+ * recorded launch adds two event records to the stream. */
+void based_timer_set_kernel_mask(based_timer* timer, unsigned mask);
 /* Waits for the recorded events and returns, for kernel `kernel_id` (0 = segment state sums,
  * 1 = segment prefix scan, 2 = chunked read-out), the number of recorded launches and their summed
  * duration in milliseconds. */

@@ -33,6 +33,7 @@ SIGNATURES = {
     "based_timer_create": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(_vp)]),
     "based_timer_destroy": (None, [_vp]),
     "based_timer_reset": (None, [_vp]),
+    "based_timer_set_kernel_mask": (None, [_vp, ctypes.c_uint]),
     "based_timer_read": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_double)]),
     "based_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),

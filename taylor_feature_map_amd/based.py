@@ -62,9 +62,11 @@ class Timer:
 
     KERNELS = (0, 1, 2)
 
-    def __init__(self, max_launches: int = 4096):
+    def __init__(self, max_launches: int = 4096, kernels=None):
         self._h = ctypes.c_void_p()
         _lib.check(_lib.lib().based_timer_create(max_launches, ctypes.byref(self._h)), "based_timer_create")
+        if kernels is not None:
+            _lib.lib().based_timer_set_kernel_mask(self._h, sum(1 << k for k in kernels))
 
     @property
     def handle(self):

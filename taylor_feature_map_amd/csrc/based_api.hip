@@ -90,6 +90,7 @@ struct based_timer {
   std::vector<int> kernel_ids;
   int capacity = 0;
   int used = 0;
+  unsigned mask = ~0u;
 };
 
 namespace {
@@ -140,13 +141,14 @@ based_status_t run(const void* q, const void* k, const void* v, const Shape& sh,
   }
 
   auto launch = [&](int id) -> hipError_t {
-    if (timer) {
+    const bool rec = timer && ((timer->mask >> id) & 1u);
+    if (rec) {
       hipError_t e = hipEventRecord(timer->events[2 * timer->used], stream);
       if (e != hipSuccess) return e;
     }
     hipError_t e = based::launch_kernel(id, q, k, v, sh, pl, sigma, wsf, out, out_f32, stream);
     if (e != hipSuccess) return e;
-    if (timer) {
+    if (rec) {
       e = hipEventRecord(timer->events[2 * timer->used + 1], stream);
       if (e != hipSuccess) return e;
       timer->kernel_ids[timer->used] = id;
@@ -257,6 +259,10 @@ void based_timer_destroy(based_timer* timer) {
 
 void based_timer_reset(based_timer* timer) {
   if (timer) timer->used = 0;
+}
+
+void based_timer_set_kernel_mask(based_timer* timer, unsigned mask) {
+  if (timer) timer->mask = mask;
 }
 
 based_status_t based_timer_read(based_timer* timer, int kernel_id, int* launches, double* total_ms) {

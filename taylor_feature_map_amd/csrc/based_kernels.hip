@@ -8,11 +8,10 @@
 // the direct polynomial (field reference_src; field perf_md describes the same split).
 //
 // Design:
-//  * Work item = (batch b, head h, 64-column slice of V, sequence segment), run by a workgroup of two
-//    wavefronts. The feature tiles (below) are split between the two waves: each wave holds its half of
-//    S in fp32 MFMA accumulators, builds only its half of phi(k) and phi(q), and the two partial
-//    read-outs are added through LDS. Each wave finishes (divides and stores) one 16-token half of the
-//    32-token chunk.
+//  * Work item = (batch b, head h, 64-column slice of V, sequence segment), run by a workgroup of W
+//    wavefronts over chunks of 32 W tokens (K = 16: W = 4; K = 8: W = 2). The feature tiles of the state
+//    are split between the waves for the update; every wave reads out two 16-token query tiles of each
+//    chunk through the whole state, whose bf16 copy the waves publish to LDS after each chunk.
 //  * The quadratic block is used in its symmetric form: the page allows any algebraic rearrangement that
 //    matches (field spec_md). Unordered feature pairs {a, b} are laid out on a 16-lane row as "cyclic
 //    distance" tiles: tile d holds x_n * x_{(n-d) mod 16} in lane n, so every partner is a DPP row
@@ -23,12 +22,14 @@
 //    fall out of the same MFMAs (field perf_md: no second matmul for the normaliser). S and z stay fp32
 //    for the whole segment (field precision_md) and are rounded to bf16 only as MFMA operands; the
 //    Taylor weights are squared in fp32 and rounded once.
-//  * Per 32-token chunk: K Q^T and the Taylor weights, the read-out phi(Q) S and the intra-chunk A V
-//    accumulate into one fp32 tile; the divide and the store are fused; then S += phi(K)^T V. phi is
+//  * Per chunk: phi(Q) S for the wave's query tiles, then per 32-token key step K Q^T, the Taylor
+//    weights and A V into the same fp32 tile, the fused divide and store, and S += phi(K)^T V. phi is
 //    built in registers and never written to memory (field perf_md names materialising it as the waste).
-//  * Inputs are prefetched one chunk ahead into registers and staged in LDS in their natural row layout
-//    (16-byte units of V swizzled against bank conflicts); the transposed MFMA operands (V and K with the
-//    token index along the contraction) come from ds_read_b64_tr_b16 transpose reads.
+//  * Global memory goes through buffer resources (32-bit per-lane offsets, the chunk advance in the
+//    scalar offset, the range check covering the ragged end of the sequence). Inputs are loaded one
+//    chunk ahead into registers and staged in LDS in their natural row layout (16-byte units of V
+//    swizzled against bank conflicts); V and K with the token index along the contraction come from
+//    ds_read_b64_tr_b16 transpose reads.
 //  * Long sequences are split into segments so that all SIMDs have work: a first kernel sums
 //    phi(k)^T v per segment, a second turns those sums into prefix states, and the read-out kernel
 //    starts each segment from its prefix state.
@@ -36,9 +37,9 @@
 // MFMA lane layouts used (v_mfma_f32_16x16x32_bf16, lane l, column c = l % 16, group g = l / 16):
 //   A operand: row c, contraction slots 8g..8g+7;  B operand: column c, slots 8g..8g+7;
 //   D: column c, rows 4g..4g+3.  The contraction order is free as long as A and B agree; slot e of
-//   group g is token 16(e/4) + 4g + e%4 of the chunk, which lets the D registers of K Q^T feed A V, and
-//   feature (t, 4g + e%4) of tile pair (t = 2m + e/4), which lets the D registers of S feed phi(Q) S,
-//   without any data movement.
+//   group g is token 16(e/4) + 4g + e%4 of a 32-token key step, which lets the D registers of K Q^T
+//   feed A V, and feature (t, 4g + e%4) of tile pair (t = 2m + e/4), which lets the D registers of S
+//   feed phi(Q) S, without any data movement.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -396,8 +397,8 @@ struct __align__(16) StateSmem {
 };
 
 template <int K, int WI>
-__device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows& rw, int64_t t_begin, int64_t t_end,
-                                                   float* __restrict__ dst) {
+__device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows& rw, int64_t T, int64_t t_begin,
+                                                   int64_t t_end, float* __restrict__ dst) {
   using SP = Split<K>;
   constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
   const int tid = threadIdx.x;
@@ -417,7 +418,7 @@ __device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows&
   int it = 0;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += SP::C, ++it) {
     const Stage<K>& st = sm.stage[it & 1];
-    pf.load(rw, t0 + SP::C);
+    pf.load(rw, t0 + SP::C < t_end ? t0 + SP::C : T);  // past the range after the last chunk: no traffic
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < SP::W; ++ks) {
@@ -453,7 +454,7 @@ __global__ __launch_bounds__(Split<K>::W * kWave) void based_segment_state_kerne
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr_for<0, Split<K>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
-    if (w == WI) segment_state_body<K, WI>(sm, rw, t_begin, t_end, dst);
+    if (w == WI) segment_state_body<K, WI>(sm, rw, sh.T, t_begin, t_end, dst);
   });
 }
 
@@ -568,8 +569,8 @@ __device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned v
 
 template <int K, int WI, bool OUT_F32>
 __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw, __amdgpu_buffer_rsrc_t ro,
-                                             unsigned out_stride, int64_t t_begin, int64_t t_end, float c1,
-                                             float c2, float sigma, const float* __restrict__ src) {
+                                             unsigned out_stride, int64_t T, int64_t t_begin, int64_t t_end,
+                                             float c1, float c2, float sigma, const float* __restrict__ src) {
   using F = Feat<K>;
   using SP = Split<K>;
   constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
@@ -615,7 +616,9 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
   pf.store(sm.stage[0], lane);
   int it = 0;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += SP::C, ++it) {
-    pf.load(rw, t0 + SP::C);
+    // After the segment's last chunk the loads are aimed past the end of the buffer range: they return
+    // zeros without touching memory.
+    pf.load(rw, t0 + SP::C < t_end ? t0 + SP::C : T);
     __syncthreads();  // this chunk's inputs and the bf16 state of earlier chunks are in LDS
     const Stage<K>& st = sm.stage[it & 1];
 
@@ -704,7 +707,7 @@ __global__ __launch_bounds__(Split<K>::W * kWave) void based_chunk_readout_kerne
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr_for<0, Split<K>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
-    if (w == WI) readout_body<K, WI, OUT_F32>(sm, rw, ro, out_stride, t_begin, t_end, c1, c2, sigma, src);
+    if (w == WI) readout_body<K, WI, OUT_F32>(sm, rw, ro, out_stride, sh.T, t_begin, t_end, c1, c2, sigma, src);
   });
 }
 

@@ -52,6 +52,7 @@ def call(q=FAKE, k=FAKE, v=FAKE, B=1, T=64, H=2, K=16, V=64, scale=math.nan, out
     (dict(K=12), _lib.BASED_ERR_UNSUPPORTED),
     (dict(V=96), _lib.BASED_ERR_UNSUPPORTED),
     (dict(V=1024), _lib.BASED_ERR_UNSUPPORTED),
+    (dict(T=1 << 20, H=16, V=128), _lib.BASED_ERR_UNSUPPORTED),  # rows exceed a 32-bit buffer range
     (dict(scale=math.inf), _lib.BASED_ERR_INVALID_ARGUMENT),
     (dict(scale=-math.inf), _lib.BASED_ERR_INVALID_ARGUMENT),
     (dict(q=FAKE + 2), _lib.BASED_ERR_INVALID_ARGUMENT),
