@@ -125,7 +125,7 @@ def run_bench(w, steps, warmup, with_cpu=True):
     out = torch.empty((w.B, w.T, w.H, w.V), dtype=out_dtype, device=dev)
     segments, seg_len, ws_bytes = plan(w.B, w.T, w.H, w.K, w.V)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    timer = Timer(max_launches=steps + 16, kernels=(2,))  # events around the read-out kernel only
+    timer = Timer(max_launches=steps + 16, kernels=(Timer.READOUT,))  # events around the read-out kernel only
 
     def step(t=None):
         based_forward(q, k, v, w.scale, out=out, workspace=ws, timer=t)

@@ -60,7 +60,8 @@ def workspace_bytes(B, T, H, K, V) -> int:
 class Timer:
     """HIP events around every kernel launched by `based_forward(..., timer=...)`."""
 
-    KERNELS = (0, 1, 2)
+    STATE, SCAN, READOUT = 0, 1, 2  # kernel ids: segment state sums, prefix scan, chunked read-out
+    KERNELS = (STATE, SCAN, READOUT)
 
     def __init__(self, max_launches: int = 4096, kernels=None):
         self._h = ctypes.c_void_p()

@@ -67,6 +67,7 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
   pl.seg_len = L;
   pl.segments = (sh.T + L - 1) / L;
   pl.slot_floats = based::state_slot_floats(sh.K);
+  pl.scanned = pl.segments > based::kMaxSummedSegments;
   return pl;
 }
 
@@ -158,10 +159,8 @@ based_status_t run(const void* q, const void* k, const void* v, const Shape& sh,
   };
 
   hipError_t e = hipSuccess;
-  if (pl.segments > 1) {
-    e = launch(0);
-    if (e == hipSuccess && pl.segments > 2) e = launch(1);
-  }
+  if (pl.segments > 1) e = launch(0);
+  if (e == hipSuccess && pl.scanned) e = launch(1);
   if (e == hipSuccess) e = launch(2);
   if (allocate && need > 0) {
     const hipError_t f = hipFreeAsync(wsf, stream);

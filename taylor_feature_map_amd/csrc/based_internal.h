@@ -17,10 +17,17 @@ struct Shape {
 };
 
 // Sequence split: `segments` pieces of `seg_len` tokens (last one possibly shorter), `nvs` value
-// slices of 64 columns, `slot_floats` floats per stored segment state.
+// slices of 64 columns, `slot_floats` floats per stored segment state sum. With `scanned` set, the
+// stored sums are turned into prefix sums by a scan kernel before the read-out; otherwise every
+// read-out adds up the sums of its predecessors itself.
 struct Plan {
   int64_t segments, seg_len, nvs, slot_floats;
+  bool scanned;
 };
+
+// Most segments for which each read-out adds up its predecessors' sums itself (beyond this, the
+// quadratic number of slot reads costs more than a scan kernel).
+constexpr int64_t kMaxSummedSegments = 16;
 
 template <int B, int E, typename F>
 __host__ __device__ __forceinline__ void constexpr_for(F&& f) {

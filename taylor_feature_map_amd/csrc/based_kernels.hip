@@ -31,15 +31,19 @@
 //    swizzled against bank conflicts); V and K with the token index along the contraction come from
 //    ds_read_b64_tr_b16 transpose reads.
 //  * Long sequences are split into segments so that all SIMDs have work: a first kernel sums
-//    phi(k)^T v per segment, a second turns those sums into prefix states, and the read-out kernel
+//    phi(k)^T v per segment (every segment but the last), and the read-out of segment g starts from
+//    the sum of the sums of segments 0 .. g - 1, added in segment order at its start. With many
+//    segments a prefix-scan kernel turns the sums into those starting states first.
 //    starts each segment from its prefix state.
 //
 // MFMA lane layouts used (v_mfma_f32_16x16x32_bf16, lane l, column c = l % 16, group g = l / 16):
 //   A operand: row c, contraction slots 8g..8g+7;  B operand: column c, slots 8g..8g+7;
 //   D: column c, rows 4g..4g+3.  The contraction order is free as long as A and B agree; slot e of
 //   group g is token 16(e/4) + 4g + e%4 of a 32-token key step, which lets the D registers of K Q^T
-//   feed A V, and feature (t, 4g + e%4) of tile pair (t = 2m + e/4), which lets the D registers of S
-//   feed phi(Q) S, without any data movement.
+//   feed the attention weights as an operand, and feature (t, 4g + e%4) of tile pair (t = 2m + e/4),
+//   which lets the D registers of S feed the read-out, without any data movement. Outputs are
+//   computed transposed (value column along the rows, token along the lanes) so that a lane holds four
+//   adjacent output columns of one token.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -355,9 +359,13 @@ __device__ __forceinline__ void load_value_operands(const Stage<K>& st, int ks, 
   vop[4] = u32x4_t{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 }
 
-// Register-native layout of one segment state in the workspace: [tile][value tile][row r][lane].
-__device__ __forceinline__ int64_t state_offset(int t, int vt, int r, int lane) {
-  return ((t * kVT + vt) * 4 + r) * kWave + lane;
+// Register-native layout of one segment state sum in the workspace, 16 bytes (the four rows r) per lane
+// and tile: the value tiles as [tile][value tile][lane][r], then the ones tile, whose 16 columns are
+// equal, as [tile][lane group][r].
+__device__ __forceinline__ int64_t state_offset(int t, int vt, int lane) { return ((t * 4 + vt) * kWave + lane) * 4; }
+template <int K>
+__device__ __forceinline__ int64_t ones_offset(int t, int g) {
+  return Feat<K>::NPT * 16 * kWave + (t * 4 + g) * 4;
 }
 
 struct ItemCoords {
@@ -433,9 +441,11 @@ __device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows&
 #pragma unroll
   for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-    for (int vt = 0; vt < kVT; ++vt)
+    for (int vt = 0; vt < 4; ++vt) *reinterpret_cast<f32x4_t*>(dst + state_offset(T0 + lt, vt, lane)) = S[lt][vt];
+  if (c == 0) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[state_offset(T0 + lt, vt, r, lane)] = S[lt][vt][r];
+    for (int lt = 0; lt < NT; ++lt) *reinterpret_cast<f32x4_t*>(dst + ones_offset<K>(T0 + lt, lane >> 4)) = S[lt][4];
+  }
 }
 
 template <int K>
@@ -460,19 +470,34 @@ __global__ __launch_bounds__(Split<K>::W * kWave) void based_segment_state_kerne
 
 // ------------------------------------------------------------- kernel 1: prefix over segments
 
-// In place: slot s of every (b, h, value slice) becomes the sum of the segment sums 0..s, i.e. the
-// state at the start of segment s + 1.
+// Used when there are too many segments for each read-out to add up its predecessors' sums: in place,
+// slot s of every (b, h, value slice) becomes the sum of the segment sums 0..s. Slots are read in batches
+// ahead of the running sum so that the loads of a batch do not wait for the stores of the previous one.
 __global__ __launch_bounds__(256) void based_segment_scan_kernel(float* __restrict__ ws, int64_t n_bhv,
                                                                  int64_t slots, int64_t slot_floats) {
+  constexpr int kBatch = 8;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= n_bhv * slot_floats) return;
   const int64_t bhv = idx / slot_floats;
   const int64_t e = idx - bhv * slot_floats;
   float* p = ws + bhv * slots * slot_floats + e;
+  float cur[kBatch];
+#pragma unroll
+  for (int j = 0; j < kBatch; ++j) cur[j] = j < slots ? p[j * slot_floats] : 0.0f;
   float run = 0.0f;
-  for (int64_t s = 0; s < slots; ++s) {
-    run += p[s * slot_floats];
-    p[s * slot_floats] = run;
+  for (int64_t s0 = 0; s0 < slots; s0 += kBatch) {
+    float nxt[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) nxt[j] = s0 + kBatch + j < slots ? p[(s0 + kBatch + j) * slot_floats] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (s0 + j < slots) {
+        run += cur[j];
+        p[(s0 + j) * slot_floats] = run;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) cur[j] = nxt[j];
   }
 }
 
@@ -501,7 +526,8 @@ __device__ __forceinline__ void publish_state(ReadoutSmem<K>& sm, const SA& S, i
 }
 
 // Intra-chunk contribution of key step ks (key tokens 32 ks .. 32 ks + 31) to 16-token query tile II:
-// scores K Q^T on the 16x16x16 MFMA, Taylor weights, then A [V | 1].
+// scores K Q^T on the 16x16x16 MFMA, Taylor weights, then the transposed product [V | 1]^T A^T, so
+// that the output tile comes out with the token along the lanes.
 template <int K, int II>
 __device__ __forceinline__ void intra_step(const Stage<K>& st, int ks, const u32x4_t (&vop)[kVT], f32x4_t (&O)[kVT],
                                            float c1, float c2, int lane) {
@@ -521,7 +547,7 @@ __device__ __forceinline__ void intra_step(const Stage<K>& st, int ks, const u32
       d[h] = mfma16(ka, qb, zero4);
     }
   }
-  // A operand: slot e <-> key token 32 ks + 16(e/4) + 4g + e%4, row (query) 16 II + c.
+  // B operand: slot e <-> key token 32 ks + 16(e/4) + 4g + e%4, column (query) 16 II + c.
   float w[8];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -539,38 +565,61 @@ __device__ __forceinline__ void intra_step(const Stage<K>& st, int ks, const u32
   }
   const u32x4_t aop = {pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7])};
 #pragma unroll
-  for (int vt = 0; vt < kVT; ++vt) O[vt] = mfma32(aop, vop[vt], O[vt]);
+  for (int vt = 0; vt < kVT; ++vt) O[vt] = mfma32(vop[vt], aop, O[vt]);
 }
 
-// o = num / (den + 1e-6) for one 16-token query tile; lane holds rows 4g + r, columns 16 vt + c.
-// voff is the lane's byte offset of (row 4g, column c); the row r and column tile vt go into the scalar
-// offset. Rows past the end of the sequence fall outside the output buffer range and are dropped.
+// o = num / (den + 1e-6) for one 16-token query tile held transposed: lane (c, g) has token c of the
+// tile and value columns 16 vt + 4 g .. 16 vt + 4 g + 3, so each value tile is one 8-byte (bf16) or
+// 16-byte (fp32) store per lane; the ones tile holds den in all four rows. voff is the lane's byte
+// offset of (token c, column 4 g); the tile's first token goes into the scalar offset. Rows past the end
+// of the sequence fall outside the output buffer range and are dropped.
 template <bool OUT_F32>
-__device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned voff, unsigned stride_bytes,
-                                           unsigned soff, const f32x4_t (&O)[kVT]) {
+__device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned voff, unsigned soff,
+                                           const f32x4_t (&O)[kVT]) {
+  const float inv = __builtin_amdgcn_rcpf(O[4][0] + 1e-6f);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float inv = __builtin_amdgcn_rcpf(O[4][r] + 1e-6f);
-    const unsigned so = soff + r * stride_bytes;
+  for (int vt = 0; vt < 4; ++vt) {
     if constexpr (OUT_F32) {
-#pragma unroll
-      for (int vt = 0; vt < 4; ++vt)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, O[vt][r] * inv), ro, voff, so + 64 * vt, 0);
+      const f32x4_t o = O[vt] * inv;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, voff, soff + 64 * vt, 0);
     } else {
-      const unsigned p01 = pack2(O[0][r] * inv, O[1][r] * inv);
-      const unsigned p23 = pack2(O[2][r] * inv, O[3][r] * inv);
-      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(p01), ro, voff, so, 0);
-      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(p01 >> 16), ro, voff, so + 32, 0);
-      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(p23), ro, voff, so + 64, 0);
-      __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(p23 >> 16), ro, voff, so + 96, 0);
+      const u32x2_t o = {pack2(O[vt][0] * inv, O[vt][1] * inv), pack2(O[vt][2] * inv, O[vt][3] * inv)};
+      __builtin_amdgcn_raw_buffer_store_b64(o, ro, voff, soff + 32 * vt, 0);
     }
+  }
+}
+
+// The state at the start of a segment: the sum, in segment order, of the state sums of the `n_src`
+// earlier segments stored at src, src + slot_floats, ...
+template <int K, int T0, int NT, typename SA>
+__device__ __forceinline__ void initial_state(SA& S, const float* __restrict__ src, int64_t n_src, int64_t slot_floats,
+                                              int lane) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int lt = 0; lt < NT; ++lt)
+#pragma unroll
+    for (int vt = 0; vt < kVT; ++vt) S[lt][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int64_t i = 0; i < n_src; ++i) {
+    const float* s = src + i * slot_floats;
+    f32x4_t x[NT][kVT];
+#pragma unroll
+    for (int lt = 0; lt < NT; ++lt) {
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt) x[lt][vt] = *reinterpret_cast<const f32x4_t*>(s + state_offset(T0 + lt, vt, lane));
+      x[lt][4] = *reinterpret_cast<const f32x4_t*>(s + ones_offset<K>(T0 + lt, g));
+    }
+#pragma unroll
+    for (int lt = 0; lt < NT; ++lt)
+#pragma unroll
+      for (int vt = 0; vt < kVT; ++vt) S[lt][vt] += x[lt][vt];
   }
 }
 
 template <int K, int WI, bool OUT_F32>
 __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw, __amdgpu_buffer_rsrc_t ro,
                                              unsigned out_stride, int64_t T, int64_t t_begin, int64_t t_end,
-                                             float c1, float c2, float sigma, const float* __restrict__ src) {
+                                             float c1, float c2, float sigma, const float* __restrict__ src,
+                                             int64_t n_src, int64_t slot_floats) {
   using F = Feat<K>;
   using SP = Split<K>;
   constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
@@ -581,22 +630,10 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
   const int c = lane & 15, g = lane >> 4;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   constexpr unsigned kOutBytes = OUT_F32 ? 4 : 2;
-  const unsigned lane_off = (4 * g) * out_stride + c * kOutBytes;
+  const unsigned lane_off = c * out_stride + 4 * g * kOutBytes;
 
   f32x4_t S[NT][kVT];
-  if (src) {
-#pragma unroll
-    for (int lt = 0; lt < NT; ++lt)
-#pragma unroll
-      for (int vt = 0; vt < kVT; ++vt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) S[lt][vt][r] = src[state_offset(T0 + lt, vt, r, lane)];
-  } else {
-#pragma unroll
-    for (int lt = 0; lt < NT; ++lt)
-#pragma unroll
-      for (int vt = 0; vt < kVT; ++vt) S[lt][vt] = zero4;
-  }
+  initial_state<K, T0, NT>(S, src, n_src, slot_floats, lane);
   publish_state<K, T0, NT>(sm, S, lane);
   if constexpr (F::NPT % 2 == 1 && T0 + NT == F::NPT) {
     // The last tile pair is half empty: its second half stays zero for the whole kernel.
@@ -622,7 +659,8 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
     __syncthreads();  // this chunk's inputs and the bf16 state of earlier chunks are in LDS
     const Stage<K>& st = sm.stage[it & 1];
 
-    // ---- read-out of earlier tokens through the state: O = phi(Q) S for this wave's two query tiles.
+    // ---- read-out of earlier tokens through the state, transposed: O^T = S^T phi(Q)^T for this wave's
+    //      two query tiles (the bf16 state tiles are the A operand, phi(Q) the B operand).
     f32x4_t O[2][kVT];
     {
       float ry[2][F::NQ], hy[2][4];
@@ -655,7 +693,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
           pq.z = pack2(F::template qval<tb, 0>(ry[ii], hy[ii], g), F::template qval<tb, 1>(ry[ii], hy[ii], g));
           pq.w = pack2(F::template qval<tb, 2>(ry[ii], hy[ii], g), F::template qval<tb, 3>(ry[ii], hy[ii], g));
 #pragma unroll
-          for (int vt = 0; vt < kVT; ++vt) O[ii][vt] = mfma32(pq, sb[vt], m == 0 ? zero4 : O[ii][vt]);
+          for (int vt = 0; vt < kVT; ++vt) O[ii][vt] = mfma32(sb[vt], pq, m == 0 ? zero4 : O[ii][vt]);
         }
       });
     }
@@ -670,8 +708,8 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
       intra_step<K, I0>(st, ks, vop, O[0], c1, c2, lane);
       intra_step<K, I1>(st, ks, vop, O[1], c1, c2, lane);
       if (ks == SP::W - 1) {
-        store_tile<OUT_F32>(ro, lane_off, out_stride, soff_out + 16 * I0 * out_stride, O[0]);
-        store_tile<OUT_F32>(ro, lane_off, out_stride, soff_out + 16 * I1 * out_stride, O[1]);
+        store_tile<OUT_F32>(ro, lane_off, soff_out + 16 * I0 * out_stride, O[0]);
+        store_tile<OUT_F32>(ro, lane_off, soff_out + 16 * I1 * out_stride, O[1]);
       }
       float kx[8];
       key_column<K>(st, ks, lane, kx);
@@ -699,15 +737,21 @@ __global__ __launch_bounds__(Split<K>::W * kWave) void based_chunk_readout_kerne
       make_rsrc(static_cast<char*>(out) + bh_v * (OUT_F32 ? 4 : 2), sh.T, out_stride);
   const int64_t t_begin = ic.g * pl.seg_len;
   const int64_t t_end = (t_begin + pl.seg_len < sh.T) ? t_begin + pl.seg_len : sh.T;
-  const float* src = nullptr;
-  if (ic.g > 0) {
-    const int64_t bhv = (ic.b * sh.H + ic.h) * pl.nvs + ic.vs;
-    src = ws + (bhv * (pl.segments - 1) + ic.g - 1) * pl.slot_floats;
+  // Initial state: the sum of the state sums of segments 0 .. g - 1, or after the prefix scan the single
+  // slot g - 1 that already holds it.
+  const int64_t bhv = (ic.b * sh.H + ic.h) * pl.nvs + ic.vs;
+  const float* src = ws + bhv * (pl.segments - 1) * pl.slot_floats;
+  int64_t n_src = ic.g;
+  if (pl.scanned && ic.g > 0) {
+    src += (ic.g - 1) * pl.slot_floats;
+    n_src = 1;
   }
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr_for<0, Split<K>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
-    if (w == WI) readout_body<K, WI, OUT_F32>(sm, rw, ro, out_stride, sh.T, t_begin, t_end, c1, c2, sigma, src);
+    if (w == WI)
+      readout_body<K, WI, OUT_F32>(sm, rw, ro, out_stride, sh.T, t_begin, t_end, c1, c2, sigma, src, n_src,
+                                   pl.slot_floats);
   });
 }
 
@@ -752,7 +796,7 @@ hipError_t launch_chunk_readout(const void* q, const void* k, const void* v, con
   return hipGetLastError();
 }
 
-int state_slot_floats(int64_t K) { return (K == 16 ? Feat<16>::NPT : Feat<8>::NPT) * kVT * 4 * kWave; }
+int state_slot_floats(int64_t K) { return (K == 16 ? Feat<16>::NPT : Feat<8>::NPT) * (16 * kWave + 16); }
 
 int chunk_tokens(int64_t K) { return K == 16 ? Split<16>::C : Split<8>::C; }
 

@@ -31,7 +31,10 @@ def test_library_exports_every_declared_symbol():
     assert lib.based_abi_version() == 1
     for s in range(6):
         assert lib.based_status_string(s)
+    assert lib.based_kernel_name(0) == b"based_segment_state_kernel"
+    assert lib.based_kernel_name(1) == b"based_segment_scan_kernel"
     assert lib.based_kernel_name(2) == b"based_chunk_readout_kernel"
+    assert lib.based_kernel_name(3) is None
     assert lib.based_kernel_name(7) is None
 
 
@@ -82,6 +85,8 @@ def test_plan():
     assert L % 32 == 0 and g == -(-8192 // L) and g * 64 >= 512
     g, L, ws = plan(1, 65000, 16, 16, 64)
     assert (g - 1) * L < 65000 <= g * L
+    g, L, ws = plan(1, 1 << 20, 1, 16, 64)
+    assert g > 16 and (g - 1) * L < (1 << 20) <= g * L
     g, L, ws = plan(1, 100, 1, 8, 64, segment_len=1000)
     assert g == 1 and ws == 0
     g, L, ws = plan(1, 100, 1, 8, 64, segment_len=33)

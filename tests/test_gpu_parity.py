@@ -67,12 +67,25 @@ def test_parity_full(B, T, H, K, V, scale, out):
 @pytest.mark.parametrize("K,V", [(16, 64), (8, 128)])
 @pytest.mark.parametrize("seg", [64, 128, 192, 256, 384, 100000])
 def test_parity_forced_segments(K, V, seg):
-    """Every sequence split (several prefix-scan steps, ragged tail, single segment) gives the answer."""
+    """Every sequence split (many earlier segment sums, ragged tail, single segment) gives the answer."""
     B, T, H = 1, 777, 2
     qb, kb, vb = make_qkv(B, T, H, K, V, seed=99 + seg)
     ref = based_ref_chunked(bf16_to_f64(qb), bf16_to_f64(kb), bf16_to_f64(vb), None, 64)
     o = _run(qb, kb, vb, None, torch.bfloat16, segment_len=seg)
     _gate(o, ref, f"K{K} V{V} seg{seg}")
+
+
+@pytest.mark.parametrize("K,V,seg", [(16, 64, 128), (8, 128, 64)])
+def test_parity_scanned_segments(K, V, seg):
+    """More than 16 segments: the segment sums go through the prefix-scan kernel first."""
+    from taylor_feature_map_amd import plan
+    B, T, H = 1, 2500, 2
+    g, _, _ = plan(B, T, H, K, V, seg)
+    assert g > 16
+    qb, kb, vb = make_qkv(B, T, H, K, V, seed=5 + seg)
+    ref = based_ref_chunked(bf16_to_f64(qb), bf16_to_f64(kb), bf16_to_f64(vb), None, 64)
+    o = _run(qb, kb, vb, None, torch.bfloat16, segment_len=seg)
+    _gate(o, ref, f"K{K} V{V} seg{seg} G{g}")
 
 
 def test_deterministic_and_split_independent():
