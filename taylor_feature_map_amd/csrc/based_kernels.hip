@@ -399,16 +399,36 @@ __device__ __forceinline__ Rows make_rows(const u16* q, const u16* k, const u16*
 
 // ------------------------------------------------------------------ kernel 0: segment state sums
 
+// The state sum of a segment is split over the W waves of the workgroup two ways: FW groups of feature
+// tiles times KW groups of key steps. Wave w owns the feature tiles of group w / KW and the key steps
+// of group w % KW of every chunk, so the waves do equal MFMA work and each reads only its own key
+// steps' values from LDS; the KW partial sums of a feature group are added at the end of the segment.
+// K = 16: 2 x 2 (5 tiles, 2 key steps per wave); K = 8: 1 x 2 (3 tiles, 1 key step per wave).
+template <int K>
+struct StateSplit {
+  static constexpr int W = Split<K>::W;
+  static constexpr int KW = 2;
+  static constexpr int FW = W / KW;
+  static constexpr int NT = Feat<K>::NPT / FW;
+  static constexpr int KS = W / KW;  // key steps per wave and chunk
+  static_assert(NT * FW == Feat<K>::NPT && KS * KW == W, "even split");
+};
+
 template <int K>
 struct __align__(16) StateSmem {
-  Stage<K> stage[2];
+  union {
+    Stage<K> stage[2];
+    f32x4_t red[StateSplit<K>::FW][StateSplit<K>::NT][kVT][kWave];  // partial sums of key-step group 1
+  };
 };
 
 template <int K, int WI>
 __device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows& rw, int64_t T, int64_t t_begin,
                                                    int64_t t_end, float* __restrict__ dst) {
   using SP = Split<K>;
-  constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
+  using SS = StateSplit<K>;
+  constexpr int FG = WI / SS::KW, KG = WI % SS::KW;
+  constexpr int T0 = FG * SS::NT, NT = SS::NT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int c = lane & 15;
@@ -429,7 +449,8 @@ __device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows&
     pf.load(rw, t0 + SP::C < t_end ? t0 + SP::C : T);  // past the range after the last chunk: no traffic
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < SP::W; ++ks) {
+    for (int j = 0; j < SS::KS; ++j) {
+      const int ks = KG * SS::KS + j;
       u32x4_t vop[kVT];
       load_value_operands<K>(st, ks, lane, vop);
       float kx[8];
@@ -438,13 +459,28 @@ __device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows&
     }
     pf.store(sm.stage[(it + 1) & 1], lane);  // read in iteration c - 1, finished before this iteration's barrier
   }
+  __syncthreads();  // the stages are free: their memory holds the partial sums now
+  if constexpr (KG == 1) {
 #pragma unroll
-  for (int lt = 0; lt < NT; ++lt)
+    for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-    for (int vt = 0; vt < 4; ++vt) *reinterpret_cast<f32x4_t*>(dst + state_offset(T0 + lt, vt, lane)) = S[lt][vt];
-  if (c == 0) {
+      for (int vt = 0; vt < kVT; ++vt) sm.red[FG][lt][vt][lane] = S[lt][vt];
+  }
+  __syncthreads();
+  if constexpr (KG == 0) {
 #pragma unroll
-    for (int lt = 0; lt < NT; ++lt) *reinterpret_cast<f32x4_t*>(dst + ones_offset<K>(T0 + lt, lane >> 4)) = S[lt][4];
+    for (int lt = 0; lt < NT; ++lt)
+#pragma unroll
+      for (int vt = 0; vt < kVT; ++vt) S[lt][vt] += sm.red[FG][lt][vt][lane];
+#pragma unroll
+    for (int lt = 0; lt < NT; ++lt)
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt) *reinterpret_cast<f32x4_t*>(dst + state_offset(T0 + lt, vt, lane)) = S[lt][vt];
+    if (c == 0) {
+#pragma unroll
+      for (int lt = 0; lt < NT; ++lt)
+        *reinterpret_cast<f32x4_t*>(dst + ones_offset<K>(T0 + lt, lane >> 4)) = S[lt][4];
+    }
   }
 }
 
