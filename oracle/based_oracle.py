@@ -17,6 +17,8 @@ Three independent routes are provided, all in float64 (or exact rationals):
   based_ref_direct    - the definition written out (library matmul for q.k and A@v).
   based_ref_chunked   - the page's chunked feature-map algorithm, in its order, explicit phi, float64 state.
   based_ref_rational  - the definition in exact rational arithmetic (fractions.Fraction), tiny shapes only.
+The chunked route also runs with its state (S, z) carried in and out (`based_ref_chunked_state`), and the
+same recurrence one token at a time (`based_ref_decode_step`): the steps on either side of the forward.
 
 Inputs are float arrays already holding bfloat16 values (decode with `bf16_to_f64`), shapes
 q, k: (B, T, H, K); v: (B, T, H, V). The result is float64 (B, T, H, V).
@@ -120,23 +122,45 @@ def phi(x):
     return np.concatenate([ones, x, quad], axis=-1)
 
 
+def feature_dim(K: int) -> int:
+    """P = 1 + K + K*K, the length of phi(x) (spec_md)."""
+    return 1 + K + K * K
+
+
 def based_ref_chunked(q, k, v, scale=None, chunk: int = 256):
     """reference_src, step for step: scale q; S = z = 0; for each chunk of `chunk` tokens:
     num = phi(q_c) S + A v_c and den = phi(q_c) z + rowsum(A) with A the causal Taylor weights of the chunk,
     o_c = num / (den + 1e-6); then S += phi(k_c)^T v_c and z += sum of phi(k_c) over the chunk.
     All (b, h) pairs are processed together; every quantity is float64."""
+    o, _ = based_ref_chunked_state(q, k, v, scale, None, chunk)
+    return o
+
+
+def based_ref_chunked_state(q, k, v, scale=None, state=None, chunk: int = 256):
+    """The algorithm of `based_ref_chunked` with its state carried across the call boundary.
+
+    reference_src starts from S = z = 0 and keeps S = sum_j phi(k_j) v_j^T (P x V) and z = sum_j phi(k_j)
+    (length P) over the tokens already processed. Here `state` = (S0, z0) of shapes (B, H, P, V) and (B, H, P),
+    in the layout of `phi` (k unscaled: the scale multiplies q only, contract_md), stands for tokens that came
+    before this call; None means no earlier tokens. Returns (o, (S, z)) with the state after the last token.
+    Processing a sequence in pieces, each starting from the state the previous piece returned, is the same
+    computation as one call over the whole sequence."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, T, H, K = q.shape
     V = v.shape[-1]
-    P = 1 + K + K * K
+    P = feature_dim(K)
     sigma = resolve_scale(scale, K)
     qh = np.transpose(q, (0, 2, 1, 3)) * sigma      # (B, H, T, K), scale multiplies q only (contract_md)
     kh = np.transpose(k, (0, 2, 1, 3))
     vh = np.transpose(v, (0, 2, 1, 3))
-    S = np.zeros((B, H, P, V))                     # sum_j phi(k_j) v_j^T over earlier chunks
-    z = np.zeros((B, H, P))                        # sum_j phi(k_j) over earlier chunks
+    if state is None:
+        S = np.zeros((B, H, P, V))                 # sum_j phi(k_j) v_j^T over earlier chunks
+        z = np.zeros((B, H, P))                    # sum_j phi(k_j) over earlier chunks
+    else:
+        S = np.array(state[0], dtype=np.float64).reshape(B, H, P, V)
+        z = np.array(state[1], dtype=np.float64).reshape(B, H, P)
     tri = np.tri(chunk, chunk)
     o = np.empty((B, H, T, V))
     for i in range(0, T, chunk):
@@ -151,7 +175,28 @@ def based_ref_chunked(q, k, v, scale=None, chunk: int = 256):
         pk = phi(kc)
         S = S + np.swapaxes(pk, -1, -2) @ vc
         z = z + pk.sum(axis=2)
-    return np.ascontiguousarray(np.transpose(o, (0, 2, 1, 3)))
+    return np.ascontiguousarray(np.transpose(o, (0, 2, 1, 3))), (S, z)
+
+
+def based_ref_decode_step(q1, k1, v1, state, scale=None):
+    """One token of the same recurrence: q1, k1 of shape (B, H, K) and v1 of shape (B, H, V) are the next
+    token of every (b, h); state = (S, z) as in `based_ref_chunked_state`. The token is folded into the state
+    first (the diagonal j = i is part of the causal sum, contract_md), then read out:
+    o = phi(scale q) S' / (phi(scale q) z' + 1e-6). Returns (o of shape (B, H, V), (S', z'))."""
+    q1 = np.asarray(q1, dtype=np.float64)
+    k1 = np.asarray(k1, dtype=np.float64)
+    v1 = np.asarray(v1, dtype=np.float64)
+    K = q1.shape[-1]
+    sigma = resolve_scale(scale, K)
+    S = np.array(state[0], dtype=np.float64)
+    z = np.array(state[1], dtype=np.float64)
+    pk = phi(k1)                                                   # (B, H, P)
+    S = S + pk[..., :, None] * v1[..., None, :]
+    z = z + pk
+    pq = phi(sigma * q1)
+    num = np.einsum("bhp,bhpv->bhv", pq, S)
+    den = np.einsum("bhp,bhp->bh", pq, z)
+    return num / (den + DEN_GUARD)[..., None], (S, z)
 
 
 # --------------------------------------------------------------------------------------------------------

@@ -11,7 +11,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import (DEN_GUARD, based_ref_chunked, based_ref_direct, based_ref_direct_rows,
+from oracle import (DEN_GUARD, based_ref_chunked, based_ref_chunked_state, based_ref_decode_step,
+                    based_ref_direct, based_ref_direct_rows, feature_dim,
                     based_ref_rational, bf16_to_f64, errors, passes_gate, phi, rational_to_f64,
                     resolve_scale, taylor_weight)
 from taylor_feature_map_amd.inputs import f32_to_bf16_bits, make_qkv
@@ -292,3 +293,107 @@ def test_errors_metric():
     o = np.array([[3.0, 4.5]])
     m, r = errors(o, ref)
     assert m == 0.5 and r == pytest.approx(0.1)
+
+
+# ------------------------------------------------ state carried in and out, and the one-token step
+
+def test_state_of_one_token_by_hand():
+    """K=2, V=1, one token k=(1,2), v=3, no earlier tokens. phi(k) = [1, k0, k1, k0k0, k0k1, k1k0, k1k1]/..
+    with the quadratic block divided by sqrt(2) (spec_md): [1, 1, 2, 1/r2, 2/r2, 2/r2, 4/r2], r2 = sqrt(2).
+    The state after it is S = phi(k) v^T = 3 phi(k) and z = phi(k). A transposed quadratic block, a missing
+    1/sqrt(2), the constant feature left out or the scale applied to k would all change an entry."""
+    r2 = np.sqrt(2.0)
+    expect_z = np.array([1.0, 1.0, 2.0, 1 / r2, 2 / r2, 2 / r2, 4 / r2])
+    q = np.array([0.5, -1.0]).reshape(1, 1, 1, 2)
+    k = np.array([1.0, 2.0]).reshape(1, 1, 1, 2)
+    v = np.array([3.0]).reshape(1, 1, 1, 1)
+    _, (S, z) = based_ref_chunked_state(q, k, v, scale=0.25)
+    np.testing.assert_allclose(z[0, 0], expect_z, rtol=1e-15)
+    np.testing.assert_allclose(S[0, 0, :, 0], 3 * expect_z, rtol=1e-15)
+    # k = (3, -1): the two off-diagonal entries are equal, the diagonal ones are k_a^2 / sqrt(2).
+    k2 = np.array([3.0, -1.0]).reshape(1, 1, 1, 2)
+    _, (S2, z2) = based_ref_chunked_state(q, k2, v, scale=0.25)
+    np.testing.assert_allclose(z2[0, 0], [1, 3, -1, 9 / r2, -3 / r2, -3 / r2, 1 / r2], rtol=1e-15)
+
+
+@pytest.mark.parametrize("K,V,cuts", [(16, 64, [100]), (8, 32, [1, 65, 200]), (4, 3, [7, 8, 9, 40])])
+def test_split_and_carry_equals_whole_sequence(K, V, cuts):
+    """Processing [0, t1), [t1, t2), ... each from the state the previous piece returned gives the outputs
+    of the definition on the whole sequence (based_ref_direct, an independent route), and the state after
+    the last piece equals the one reached in a single call."""
+    B, T, H = 2, 257, 2
+    q, k, v = qkv(B, T, H, K, V, seed=K + V)
+    whole = based_ref_direct(q, k, v)
+    state = None
+    pieces = []
+    bounds = [0] + cuts + [T]
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        o, state = based_ref_chunked_state(q[:, a:b], k[:, a:b], v[:, a:b], None, state, chunk=64)
+        pieces.append(o)
+    np.testing.assert_allclose(np.concatenate(pieces, axis=1), whole, rtol=0, atol=1e-12)
+    _, (S1, z1) = based_ref_chunked_state(q, k, v, None, None, chunk=64)
+    np.testing.assert_allclose(state[0], S1, rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(state[1], z1, rtol=1e-12, atol=1e-9)
+    # z's constant feature counts the tokens, its linear block sums k (spec_md's phi).
+    np.testing.assert_allclose(z1[..., 0], T, rtol=0, atol=0)
+    np.testing.assert_allclose(z1[..., 1:1 + K], np.transpose(k.sum(axis=1), (0, 1, 2)), rtol=1e-12, atol=1e-9)
+
+
+def test_state_readout_is_definition_for_any_prefix():
+    """The state read-out phi(scale q) S / (phi(scale q) z + 1e-6) for a query after the prefix equals the
+    definition restricted to the prefix plus that query's own token: checks S, z against spec_md's sum."""
+    B, T, H, K, V = 1, 50, 1, 4, 5
+    q, k, v = qkv(B, T, H, K, V, seed=11)
+    sigma = resolve_scale(None, K)
+    _, (S, z) = based_ref_chunked_state(q[:, :T - 1], k[:, :T - 1], v[:, :T - 1], None, None, chunk=16)
+    pq = phi(sigma * q[0, T - 1, 0])
+    s_last = sigma * float(q[0, T - 1, 0] @ k[0, T - 1, 0])
+    a_last = taylor_weight(s_last)
+    num = pq @ S[0, 0] + a_last * v[0, T - 1, 0]
+    den = pq @ z[0, 0] + a_last
+    np.testing.assert_allclose(num / (den + DEN_GUARD), based_ref_direct(q, k, v)[0, T - 1, 0], rtol=1e-12)
+
+
+@pytest.mark.parametrize("K,V", [(16, 64), (8, 16)])
+def test_decode_steps_equal_definition(K, V):
+    """Prefill of 37 tokens with the state carried out, then one decode step per remaining token: every
+    output equals the definition on the whole sequence, the diagonal included (contract_md)."""
+    B, T, H = 2, 45, 3
+    q, k, v = qkv(B, T, H, K, V, seed=3 * K)
+    whole = based_ref_direct(q, k, v)
+    o, state = based_ref_chunked_state(q[:, :37], k[:, :37], v[:, :37], None, None, chunk=16)
+    np.testing.assert_allclose(o, whole[:, :37], rtol=0, atol=1e-12)
+    for t in range(37, T):
+        o1, state = based_ref_decode_step(q[:, t], k[:, t], v[:, t], state)
+        np.testing.assert_allclose(o1, whole[:, t], rtol=0, atol=1e-12)
+
+
+def test_decode_from_empty_state_first_token_is_v():
+    """With no earlier tokens the first output is v itself up to the guard: A/(A + 1e-6) v (spec_md)."""
+    K, V = 8, 4
+    q, k, v = qkv(1, 1, 2, K, V, seed=1)
+    P = feature_dim(K)
+    state = (np.zeros((1, 2, P, V)), np.zeros((1, 2, P)))
+    o, _ = based_ref_decode_step(q[:, 0], k[:, 0], v[:, 0], state)
+    a = taylor_weight(resolve_scale(None, K) * np.einsum("bhk,bhk->bh", q[:, 0], k[:, 0]))
+    np.testing.assert_allclose(o, v[:, 0] * (a / (a + DEN_GUARD))[..., None], rtol=1e-14)
+
+
+def test_antisymmetric_state_part_does_not_change_outputs():
+    """phi(q) . S only sees the symmetric part of the quadratic block (q_a q_b = q_b q_a): adding an
+    antisymmetric matrix to that block of S0 and z0 leaves every output unchanged. A kernel that keeps only
+    unordered feature pairs must therefore fold S0[(a,b)] + S0[(b,a)] when it imports a state."""
+    B, T, H, K, V = 1, 20, 2, 4, 3
+    q, k, v = qkv(B, T, H, K, V, seed=21)
+    _, st = based_ref_chunked_state(q[:, :8], k[:, :8], v[:, :8], None, None)
+    o_ref, _ = based_ref_chunked_state(q[:, 8:], k[:, 8:], v[:, 8:], None, st)
+    rng = np.random.default_rng(0)
+    M = rng.standard_normal((B, H, K, K, V))
+    anti = (M - np.swapaxes(M, 2, 3)).reshape(B, H, K * K, V)
+    m = rng.standard_normal((B, H, K, K))
+    anti_z = (m - np.swapaxes(m, 2, 3)).reshape(B, H, K * K)
+    S0, z0 = st[0].copy(), st[1].copy()
+    S0[:, :, 1 + K:] += anti
+    z0[:, :, 1 + K:] += anti_z
+    o, _ = based_ref_chunked_state(q[:, 8:], k[:, 8:], v[:, 8:], None, (S0, z0))
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
