@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 1
+#define BASED_ABI_VERSION 2
 
 typedef enum {
     BASED_OK = 0,
@@ -88,6 +88,57 @@ based_status_t based_forward_ws(const void* q, const void* k, const void* v,
                                 int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                 float scale, void* out, based_dtype_t out_dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------------
+ * State on either side of the forward: carried in and out, and the one-token recurrent step.
+ *
+ * The page's reference (field reference_src) keeps, for every (b, h), the state of the tokens processed so
+ * far: S = sum_j phi(k_j) v_j^T, a P x V matrix, and z = sum_j phi(k_j), a length-P vector, with
+ * phi(x) = [1, x, x (x) x / sqrt(2)] (field spec_md), P = 1 + K + K^2, k unscaled (the scale multiplies q
+ * only, field contract_md). Layout, fp32, row-major, contiguous: S of (B, H, P, V), element (b, h, r, c)
+ * at ((b*H + h)*P + r)*V + c; z of (B, H, P). Row 0 is the constant feature, rows 1 .. K the linear
+ * block, row 1 + K + a*K + b holds x_a x_b / sqrt(2). The page grades the forward alone (field
+ * contract_md excludes an initial state); these entry points are the steps on either side of it.
+ * ------------------------------------------------------------------------------------------------- */
+
+/* P = 1 + K + K^2: rows of the state for feature dimension K. */
+int64_t based_feature_dim(int64_t K);
+
+/*
+ * based_forward with a state: the tokens are read out as if preceded by the tokens that produced
+ * (state_in, norm_in), and the state after the last token is written to (state_out, norm_out).
+ *   state_in, norm_in   : device, read-only, (B, H, P, V) and (B, H, P) fp32, or both NULL (no earlier
+ *                         tokens). Only the symmetric part of the quadratic block can reach an output
+ *                         (phi(q) . S weighs rows (a, b) and (b, a) alike), and only that part is read.
+ *   state_out, norm_out : device, (B, H, P, V) and (B, H, P) fp32, fully written, or both NULL. The two
+ *                         rows of an off-diagonal pair come out equal. Must not overlap any other argument
+ *                         (in particular state_out may not alias state_in: carry state through a second
+ *                         buffer).
+ *   workspace           : as in based_forward_ws, or NULL to allocate it stream-ordered as based_forward does.
+ * Splitting a sequence into pieces, each called with the state the previous piece returned, gives the
+ * outputs and final state of one call over the whole sequence (up to rounding).
+ */
+based_status_t based_forward_state(const void* q, const void* k, const void* v,
+                                   int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                   float scale, void* out, based_dtype_t out_dtype,
+                                   const float* state_in, const float* norm_in,
+                                   float* state_out, float* norm_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One token of the recurrence for every (b, h): the token is folded into the state first (the causal
+ * sum includes the diagonal, field contract_md), then read out:
+ *     S += phi(k) v^T,  z += phi(k),  o = phi(scale q) S / (phi(scale q) z + 1e-6).
+ *   q, k  : device, (B, H, K) bf16 (one token; the same bytes as a (B, 1, H, K) tensor)
+ *   v     : device, (B, H, V) bf16
+ *   state, norm : device, (B, H, P, V) and (B, H, P) fp32, updated in place (layout above)
+ *   out   : device, (B, H, V), bf16 (round to nearest even) or fp32
+ * Supported K and V as for based_forward. Asynchronous on `stream`; no allocation.
+ */
+based_status_t based_decode_step(const void* q, const void* k, const void* v,
+                                 int64_t B, int64_t H, int64_t K, int64_t V,
+                                 float scale, float* state, float* norm,
+                                 void* out, based_dtype_t out_dtype, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------------
  * Execution plan and instrumentation (same operation; for tests and measurement).

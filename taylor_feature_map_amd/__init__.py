@@ -2,4 +2,4 @@
 
 The compute path lives in libbased.so (include/based.h); this package is its thin Python binding.
 """
-from .based import Timer, based_forward, plan, workspace_bytes  # noqa: F401
+from .based import Timer, based_decode_step, based_forward, feature_dim, plan, workspace_bytes  # noqa: F401

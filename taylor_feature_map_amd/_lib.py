@@ -39,6 +39,11 @@ SIGNATURES = {
     "based_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
     "based_forward_ex": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp,
                                         ctypes.c_int, _vp, ctypes.c_size_t, _i64, _vp, _vp]),
+    "based_feature_dim": (_i64, [_i64]),
+    "based_forward_state": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp,
+                                           ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "based_decode_step": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_float, _vp, _vp, _vp,
+                                         ctypes.c_int, _vp]),
 }
 
 _lib = None

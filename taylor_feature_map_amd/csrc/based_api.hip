@@ -98,7 +98,7 @@ namespace {
 
 based_status_t run(const void* q, const void* k, const void* v, const Shape& sh, float scale, void* out,
                    based_dtype_t out_dtype, void* ws, size_t ws_bytes, int64_t seg_override, based_timer* timer,
-                   hipStream_t stream, bool allocate) {
+                   hipStream_t stream, bool allocate, const based::StateIO& io = based::StateIO{}) {
   if (based_status_t s = check_shape(sh.B, sh.T, sh.H, sh.K, sh.V)) return s;
   if (!q || !k || !v || !out) return fail(BASED_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (out_dtype != BASED_BF16 && out_dtype != BASED_F32)
@@ -116,6 +116,29 @@ based_status_t run(const void* q, const void* k, const void* v, const Shape& sh,
   if (overlaps(out, o_bytes, q, qk_bytes) || overlaps(out, o_bytes, k, qk_bytes) ||
       overlaps(out, o_bytes, v, v_bytes))
     return fail(BASED_ERR_INVALID_ARGUMENT, "out overlaps an input");
+  const int64_t P = 1 + sh.K + sh.K * sh.K;
+  const size_t s_bytes = static_cast<size_t>(sh.B * sh.H * P * sh.V) * 4;
+  const size_t z_bytes = static_cast<size_t>(sh.B * sh.H * P) * 4;
+  if (!io.s_in != !io.z_in) return fail(BASED_ERR_INVALID_ARGUMENT, "state_in and norm_in must both be set or both NULL");
+  if (!io.s_out != !io.z_out)
+    return fail(BASED_ERR_INVALID_ARGUMENT, "state_out and norm_out must both be set or both NULL");
+  if ((io.s_in && (!aligned16(io.s_in) || !aligned16(io.z_in))) ||
+      (io.s_out && (!aligned16(io.s_out) || !aligned16(io.z_out))))
+    return fail(BASED_ERR_INVALID_ARGUMENT, "state pointers must be 16-byte aligned");
+  if (io.s_out) {
+    const void* outs[2] = {io.s_out, io.z_out};
+    const size_t outn[2] = {s_bytes, z_bytes};
+    const void* others[6] = {q, k, v, out, io.s_in, io.z_in};
+    const size_t othern[6] = {qk_bytes, qk_bytes, v_bytes, o_bytes, io.s_in ? s_bytes : 0, io.z_in ? z_bytes : 0};
+    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 6; ++j)
+        if (overlaps(outs[i], outn[i], others[j], othern[j]))
+          return fail(BASED_ERR_INVALID_ARGUMENT, "state_out / norm_out overlap an input, out or the state input");
+    if (overlaps(io.s_out, s_bytes, io.z_out, z_bytes))
+      return fail(BASED_ERR_INVALID_ARGUMENT, "state_out and norm_out overlap");
+  }
+  if (io.s_in && (overlaps(out, o_bytes, io.s_in, s_bytes) || overlaps(out, o_bytes, io.z_in, z_bytes)))
+    return fail(BASED_ERR_INVALID_ARGUMENT, "out overlaps the state input");
 
   const Plan pl = make_plan(sh, seg_override);
   const size_t need = workspace_bytes(sh, pl);
@@ -126,7 +149,9 @@ based_status_t run(const void* q, const void* k, const void* v, const Shape& sh,
                   "workspace has " + std::to_string(ws_bytes) + " bytes, needs " + std::to_string(need));
     if (need > 0 && !aligned16(ws)) return fail(BASED_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     if (overlaps(out, o_bytes, ws, need) || overlaps(ws, need, q, qk_bytes) || overlaps(ws, need, k, qk_bytes) ||
-        overlaps(ws, need, v, v_bytes))
+        overlaps(ws, need, v, v_bytes) || overlaps(ws, need, io.s_in, io.s_in ? s_bytes : 0) ||
+        overlaps(ws, need, io.z_in, io.z_in ? z_bytes : 0) || overlaps(ws, need, io.s_out, io.s_out ? s_bytes : 0) ||
+        overlaps(ws, need, io.z_out, io.z_out ? z_bytes : 0))
       return fail(BASED_ERR_INVALID_ARGUMENT, "workspace overlaps a tensor");
   }
 
@@ -147,7 +172,7 @@ based_status_t run(const void* q, const void* k, const void* v, const Shape& sh,
       hipError_t e = hipEventRecord(timer->events[2 * timer->used], stream);
       if (e != hipSuccess) return e;
     }
-    hipError_t e = based::launch_kernel(id, q, k, v, sh, pl, sigma, wsf, out, out_f32, stream);
+    hipError_t e = based::launch_kernel(id, q, k, v, sh, pl, sigma, wsf, out, out_f32, io, stream);
     if (e != hipSuccess) return e;
     if (rec) {
       e = hipEventRecord(timer->events[2 * timer->used + 1], stream);
@@ -228,6 +253,46 @@ based_status_t based_forward_ex(const void* q, const void* k, const void* v, int
                                 based_timer* timer, hipStream_t stream) {
   return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, workspace, workspace_bytes, segment_len_override,
              timer, stream, false);
+}
+
+int64_t based_feature_dim(int64_t K) { return 1 + K + K * K; }
+
+based_status_t based_forward_state(const void* q, const void* k, const void* v, int64_t B, int64_t T, int64_t H,
+                                   int64_t K, int64_t V, float scale, void* out, based_dtype_t out_dtype,
+                                   const float* state_in, const float* norm_in, float* state_out, float* norm_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const based::StateIO io{state_in, norm_in, state_out, norm_out};
+  return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, workspace, workspace_bytes, 0, nullptr, stream,
+             workspace == nullptr, io);
+}
+
+based_status_t based_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t K,
+                                 int64_t V, float scale, float* state, float* norm, void* out,
+                                 based_dtype_t out_dtype, hipStream_t stream) {
+  if (based_status_t s = check_shape(B, 1, H, K, V)) return s;
+  if (!q || !k || !v || !out || !state || !norm) return fail(BASED_ERR_INVALID_ARGUMENT, "null pointer");
+  if (out_dtype != BASED_BF16 && out_dtype != BASED_F32)
+    return fail(BASED_ERR_INVALID_ARGUMENT, "out_dtype must be BASED_BF16 or BASED_F32");
+  if (std::isinf(scale)) return fail(BASED_ERR_INVALID_ARGUMENT, "scale must be finite (NaN selects K**-0.5)");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state) || !aligned16(norm))
+    return fail(BASED_ERR_INVALID_ARGUMENT, "device pointers must be 16-byte aligned");
+  const int64_t P = 1 + K + K * K;
+  const size_t s_bytes = static_cast<size_t>(B * H * P * V) * 4, z_bytes = static_cast<size_t>(B * H * P) * 4;
+  const size_t qk_bytes = static_cast<size_t>(B * H * K) * 2, v_bytes = static_cast<size_t>(B * H * V) * 2;
+  const size_t o_bytes = static_cast<size_t>(B * H * V) * (out_dtype == BASED_F32 ? 4 : 2);
+  const void* ptrs[4] = {q, k, v, out};
+  const size_t sizes[4] = {qk_bytes, qk_bytes, v_bytes, o_bytes};
+  for (int j = 0; j < 4; ++j)
+    if (overlaps(state, s_bytes, ptrs[j], sizes[j]) || overlaps(norm, z_bytes, ptrs[j], sizes[j]))
+      return fail(BASED_ERR_INVALID_ARGUMENT, "state / norm overlap an input or out");
+  if (overlaps(state, s_bytes, norm, z_bytes)) return fail(BASED_ERR_INVALID_ARGUMENT, "state and norm overlap");
+  if (overlaps(out, o_bytes, q, qk_bytes) || overlaps(out, o_bytes, k, qk_bytes) || overlaps(out, o_bytes, v, v_bytes))
+    return fail(BASED_ERR_INVALID_ARGUMENT, "out overlaps an input");
+  const float sigma = std::isnan(scale) ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(K))) : scale;
+  const hipError_t e =
+      based::launch_decode_step(q, k, v, B, H, K, V, sigma, state, norm, out, out_dtype == BASED_F32, stream);
+  if (e != hipSuccess) return fail(BASED_ERR_HIP, std::string("HIP: ") + hipGetErrorString(e));
+  return ok();
 }
 
 based_status_t based_timer_create(int max_launches, based_timer** timer) {

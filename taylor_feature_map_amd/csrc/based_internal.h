@@ -43,8 +43,24 @@ int state_slot_floats(int64_t K);
 // segment lengths are multiples of it.
 int chunk_tokens(int64_t K);
 
+// Optional state in the page's layout, fp32: S of (B, H, P, V) and z of (B, H, P), P = 1 + K + K^2. The
+// read-out adds s_in / z_in to its starting state and writes the state after the last token to s_out /
+// z_out (either pair may be null).
+struct StateIO {
+  const float* s_in;
+  const float* z_in;
+  float* s_out;
+  float* z_out;
+};
+
 // kernel_id: 0 = segment state sums, 1 = prefix over segments, 2 = chunked read-out.
 hipError_t launch_kernel(int kernel_id, const void* q, const void* k, const void* v, const Shape& sh,
-                         const Plan& pl, float sigma, float* ws, void* out, bool out_f32, hipStream_t stream);
+                         const Plan& pl, float sigma, float* ws, void* out, bool out_f32, const StateIO& io,
+                         hipStream_t stream);
+
+// One-token recurrent step on (B, H) rows of q, k (K) and v (V), state S (B, H, P, V) and z (B, H, P) updated
+// in place.
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t K,
+                              int64_t V, float sigma, float* S, float* z, void* out, bool out_f32, hipStream_t stream);
 
 }  // namespace based

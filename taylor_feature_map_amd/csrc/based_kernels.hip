@@ -191,6 +191,67 @@ struct Feat<8> {
   }
 };
 
+// Feature (tile t, row n) of the kernels against the rows of the page's phi (field spec_md): row 0 is the
+// constant, rows 1 .. K the linear block, row 1 + K + a K + b holds x_a x_b / sqrt(2). The kernels keep
+// each unordered pair {a, b} once, unscaled (the query side carries the coefficients), so a state in the
+// page's layout maps to them as: constant and linear rows as they are, diagonal (a, a) times sqrt(2), and
+// pair {a, b} as (row (a, b) + row (b, a)) / sqrt(2); the other way round both rows of a pair get the
+// kernel value / sqrt(2). Only the symmetric part of an imported quadratic block can reach an output.
+enum : int { kFeatNone = 0, kFeatConst = 1, kFeatLin = 2, kFeatDiag = 3, kFeatPair = 4 };
+struct FeatRows {
+  int kind, a, b;
+};
+constexpr float kSqrt2 = 1.41421356237309515f;
+constexpr float kRSqrt2 = 0.707106781186547573f;
+
+template <int K>
+__device__ __forceinline__ FeatRows feat_rows(int t, int n) {
+  if constexpr (K == 16) {
+    if (t == 0) return {kFeatDiag, n, n};
+    if (t <= 7) return {kFeatPair, n, (n - t) & 15};
+    if (t == 8) return n < 8 ? FeatRows{kFeatPair, n, n + 8} : FeatRows{n == 8 ? kFeatConst : kFeatNone, 0, 0};
+    return {kFeatLin, n, n};
+  } else {
+    const int f = n & 7, h = n >> 3;
+    if (t == 0) return h == 0 ? FeatRows{kFeatDiag, f, f} : FeatRows{kFeatPair, f, (f - 1) & 7};
+    if (t == 1) return {kFeatPair, f, (f - (h == 0 ? 2 : 3)) & 7};
+    if (h == 1) return {kFeatLin, f, f};
+    return f < 4 ? FeatRows{kFeatPair, f, f + 4} : FeatRows{f == 4 ? kFeatConst : kFeatNone, 0, 0};
+  }
+}
+
+template <int K>
+__device__ __forceinline__ int quad_row(int a, int b) {
+  return 1 + K + a * K + b;
+}
+
+// Kernel value of a feature from a state in the page's layout; x(row) reads the lane's entry of a row.
+template <int K, typename X>
+__device__ __forceinline__ float import_feature(const FeatRows& fr, X x) {
+  switch (fr.kind) {
+    case kFeatConst: return x(0);
+    case kFeatLin: return x(1 + fr.a);
+    case kFeatDiag: return kSqrt2 * x(quad_row<K>(fr.a, fr.a));
+    case kFeatPair: return (x(quad_row<K>(fr.a, fr.b)) + x(quad_row<K>(fr.b, fr.a))) * kRSqrt2;
+    default: return 0.0f;
+  }
+}
+
+// Writes a kernel feature value into the page's layout; w(row, value) stores the lane's entry of a row.
+template <int K, typename Wr>
+__device__ __forceinline__ void export_feature(const FeatRows& fr, float val, Wr w) {
+  switch (fr.kind) {
+    case kFeatConst: w(0, val); break;
+    case kFeatLin: w(1 + fr.a, val); break;
+    case kFeatDiag: w(quad_row<K>(fr.a, fr.a), val * kRSqrt2); break;
+    case kFeatPair:
+      w(quad_row<K>(fr.a, fr.b), val * kRSqrt2);
+      w(quad_row<K>(fr.b, fr.a), val * kRSqrt2);
+      break;
+    default: break;
+  }
+}
+
 // ----------------------------------------------------------------------------- work split
 
 // One work item (b, h, value slice, segment) runs on a workgroup of W waves over chunks of C = 32 W
@@ -651,11 +712,64 @@ __device__ __forceinline__ void initial_state(SA& S, const float* __restrict__ s
   }
 }
 
+// A state in the page's layout for one (b, h) and value slice: entry (row r, slice column j) of S at
+// s[r * V + j], of z at z[r]. Import when s_in is set, export (of the state after the last token) when
+// s_out is set; write_z selects the one value slice that writes z.
+struct StateView {
+  const float* s_in;
+  const float* z_in;
+  float* s_out;
+  float* z_out;
+  int64_t V;
+  bool write_z;
+};
+
+template <int K, int T0, int NT, typename SA>
+__device__ __forceinline__ void import_state(SA& S, const StateView& sv, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int lt = 0; lt < NT; ++lt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const FeatRows fr = feat_rows<K>(T0 + lt, 4 * g + r);
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt) {
+        const float* col = sv.s_in + 16 * vt + c;
+        S[lt][vt][r] += import_feature<K>(fr, [&](int row) { return col[row * sv.V]; });
+      }
+      S[lt][4][r] += import_feature<K>(fr, [&](int row) { return sv.z_in[row]; });
+    }
+  }
+}
+
+// The padding tokens of a ragged last chunk (k = v = 0, so phi(k) = [1, 0, ...]) added `n_pad` to the
+// constant feature of z and nothing else; the exported z leaves them out.
+template <int K, int T0, int NT, typename SA>
+__device__ __forceinline__ void export_state(const SA& S, const StateView& sv, float n_pad, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int lt = 0; lt < NT; ++lt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const FeatRows fr = feat_rows<K>(T0 + lt, 4 * g + r);
+#pragma unroll
+      for (int vt = 0; vt < 4; ++vt) {
+        float* col = sv.s_out + 16 * vt + c;
+        export_feature<K>(fr, S[lt][vt][r], [&](int row, float x) { col[row * sv.V] = x; });
+      }
+      if (sv.write_z && c == 0) {
+        const float zv = fr.kind == kFeatConst ? S[lt][4][r] - n_pad : S[lt][4][r];
+        export_feature<K>(fr, zv, [&](int row, float x) { sv.z_out[row] = x; });
+      }
+    }
+  }
+}
+
 template <int K, int WI, bool OUT_F32>
 __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw, __amdgpu_buffer_rsrc_t ro,
                                              unsigned out_stride, int64_t T, int64_t t_begin, int64_t t_end,
                                              float c1, float c2, float sigma, const float* __restrict__ src,
-                                             int64_t n_src, int64_t slot_floats) {
+                                             int64_t n_src, int64_t slot_floats, const StateView& sv) {
   using F = Feat<K>;
   using SP = Split<K>;
   constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
@@ -670,6 +784,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
 
   f32x4_t S[NT][kVT];
   initial_state<K, T0, NT>(S, src, n_src, slot_floats, lane);
+  if (sv.s_in) import_state<K, T0, NT>(S, sv, lane);
   publish_state<K, T0, NT>(sm, S, lane);
   if constexpr (F::NPT % 2 == 1 && T0 + NT == F::NPT) {
     // The last tile pair is half empty: its second half stays zero for the whole kernel.
@@ -755,12 +870,16 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
     publish_state<K, T0, NT>(sm, S, lane);
     pf.store(sm.stage[(it + 1) & 1], lane);  // that buffer's chunk c - 1 was finished before the last barrier
   }
+  if (sv.s_out && t_end == T) {
+    const int64_t n = t_end - t_begin;
+    export_state<K, T0, NT>(S, sv, static_cast<float>((n + SP::C - 1) / SP::C * SP::C - n), lane);
+  }
 }
 
 template <int K, bool OUT_F32>
 __global__ __launch_bounds__(Split<K>::W * kWave) void based_chunk_readout_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float c1,
-    float c2, float sigma, const float* __restrict__ ws, void* __restrict__ out) {
+    float c2, float sigma, const float* __restrict__ ws, void* __restrict__ out, StateIO io) {
   const int64_t item = item_of_block();
   const int64_t items = sh.B * sh.H * pl.nvs * pl.segments;
   if (item >= items) return;
@@ -782,13 +901,88 @@ __global__ __launch_bounds__(Split<K>::W * kWave) void based_chunk_readout_kerne
     src += (ic.g - 1) * pl.slot_floats;
     n_src = 1;
   }
+  StateView sv;
+  const int64_t P = 1 + K + K * K;
+  const int64_t bh = ic.b * sh.H + ic.h;
+  sv.s_in = io.s_in ? io.s_in + bh * P * sh.V + ic.vs * kVSlice : nullptr;
+  sv.z_in = io.z_in ? io.z_in + bh * P : nullptr;
+  sv.s_out = io.s_out ? io.s_out + bh * P * sh.V + ic.vs * kVSlice : nullptr;
+  sv.z_out = io.z_out ? io.z_out + bh * P : nullptr;
+  sv.V = sh.V;
+  sv.write_z = ic.vs == 0;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr_for<0, Split<K>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
     if (w == WI)
       readout_body<K, WI, OUT_F32>(sm, rw, ro, out_stride, sh.T, t_begin, t_end, c1, c2, sigma, src, n_src,
-                                   pl.slot_floats);
+                                   pl.slot_floats, sv);
   });
+}
+
+// -------------------------------------------------------------- kernel 3: one-token recurrent step
+
+// phi of the page (field spec_md), row r of P = 1 + K + K^2: 1, x_{r-1}, or x_a x_b / sqrt(2).
+template <int K>
+__device__ __forceinline__ float phi_row(const float* x, int r) {
+  if (r == 0) return 1.0f;
+  if (r <= K) return x[r - 1];
+  const int i = r - 1 - K;
+  return x[i / K] * x[i % K] * kRSqrt2;
+}
+
+// One workgroup per (b, h): S += phi(k) v^T and z += phi(k) in place (the page's layout, fp32), then
+// o = phi(scale q) S / (phi(scale q) z + 1e-6). Memory-bound: every state entry is read and written once.
+template <int K>
+__global__ __launch_bounds__(256) void based_decode_step_kernel(const u16* __restrict__ q, const u16* __restrict__ k,
+                                                                const u16* __restrict__ v, int64_t V, float sigma,
+                                                                float* __restrict__ S, float* __restrict__ z,
+                                                                void* __restrict__ out, bool out_f32) {
+  constexpr int P = 1 + K + K * K;
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ float sq[K], sk[K], part_num[4][64], part_den[256], den_total;
+  if (tid < K) {
+    sq[tid] = sigma * lo_f(q[bh * K + tid]);
+    sk[tid] = lo_f(k[bh * K + tid]);
+  }
+  __syncthreads();
+  float* Sb = S + bh * P * V;
+  float* zb = z + bh * P;
+  float dp = 0.0f;
+  for (int r = tid; r < P; r += 256) {
+    const float nz = zb[r] + phi_row<K>(sk, r);
+    zb[r] = nz;
+    dp += phi_row<K>(sq, r) * nz;
+  }
+  part_den[tid] = dp;
+  __syncthreads();
+  if (tid == 0) {
+    float d = 0.0f;
+    for (int i = 0; i < 256; ++i) d += part_den[i];
+    den_total = d;
+  }
+  const int cl = tid & 63, part = tid >> 6;
+  for (int64_t c0 = 0; c0 < V; c0 += 64) {
+    const int64_t col = c0 + cl;
+    const float vv = lo_f(v[bh * V + col]);
+    float num = 0.0f;
+    for (int r = part; r < P; r += 4) {
+      const float sn = Sb[r * V + col] + phi_row<K>(sk, r) * vv;
+      Sb[r * V + col] = sn;
+      num += phi_row<K>(sq, r) * sn;
+    }
+    part_num[part][cl] = num;
+    __syncthreads();  // also publishes den_total on the first pass
+    if (part == 0) {
+      const float o = (((part_num[0][cl] + part_num[1][cl]) + part_num[2][cl]) + part_num[3][cl]) / (den_total + 1e-6f);
+      if (out_f32) {
+        static_cast<float*>(out)[bh * V + col] = o;
+      } else {
+        static_cast<u16*>(out)[bh * V + col] = static_cast<u16>(pack2(o, 0.0f) & 0xffffu);
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------------------------- host launchers
@@ -815,7 +1009,8 @@ hipError_t launch_segment_scan(const Shape& sh, const Plan& pl, float* ws, hipSt
 
 template <int K>
 hipError_t launch_chunk_readout(const void* q, const void* k, const void* v, const Shape& sh, const Plan& pl,
-                                float sigma, const float* ws, void* out, bool out_f32, hipStream_t stream) {
+                                float sigma, const float* ws, void* out, bool out_f32, const StateIO& io,
+                                hipStream_t stream) {
   const int64_t items = sh.B * sh.H * pl.nvs * pl.segments;
   const int64_t blocks = (items + 7) / 8 * 8;
   const float c1 = sigma;
@@ -823,11 +1018,24 @@ hipError_t launch_chunk_readout(const void* q, const void* k, const void* v, con
   if (out_f32) {
     hipLaunchKernelGGL((based_chunk_readout_kernel<K, true>), dim3(static_cast<unsigned>(blocks)),
                        dim3(Split<K>::W * kWave), 0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                       static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out);
+                       static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out, io);
   } else {
     hipLaunchKernelGGL((based_chunk_readout_kernel<K, false>), dim3(static_cast<unsigned>(blocks)),
                        dim3(Split<K>::W * kWave), 0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                       static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out);
+                       static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out, io);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t K,
+                              int64_t V, float sigma, float* S, float* z, void* out, bool out_f32, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(B * H)), block(256);
+  if (K == 16) {
+    hipLaunchKernelGGL(based_decode_step_kernel<16>, grid, block, 0, stream, static_cast<const u16*>(q),
+                       static_cast<const u16*>(k), static_cast<const u16*>(v), V, sigma, S, z, out, out_f32);
+  } else {
+    hipLaunchKernelGGL(based_decode_step_kernel<8>, grid, block, 0, stream, static_cast<const u16*>(q),
+                       static_cast<const u16*>(k), static_cast<const u16*>(v), V, sigma, S, z, out, out_f32);
   }
   return hipGetLastError();
 }
@@ -837,7 +1045,8 @@ int state_slot_floats(int64_t K) { return (K == 16 ? Feat<16>::NPT : Feat<8>::NP
 int chunk_tokens(int64_t K) { return K == 16 ? Split<16>::C : Split<8>::C; }
 
 hipError_t launch_kernel(int kernel_id, const void* q, const void* k, const void* v, const Shape& sh,
-                         const Plan& pl, float sigma, float* ws, void* out, bool out_f32, hipStream_t stream) {
+                         const Plan& pl, float sigma, float* ws, void* out, bool out_f32, const StateIO& io,
+                         hipStream_t stream) {
   switch (kernel_id) {
     case 0:
       return sh.K == 16 ? launch_segment_state<16>(k, v, sh, pl, ws, stream)
@@ -845,8 +1054,8 @@ hipError_t launch_kernel(int kernel_id, const void* q, const void* k, const void
     case 1:
       return launch_segment_scan(sh, pl, ws, stream);
     default:
-      return sh.K == 16 ? launch_chunk_readout<16>(q, k, v, sh, pl, sigma, ws, out, out_f32, stream)
-                        : launch_chunk_readout<8>(q, k, v, sh, pl, sigma, ws, out, out_f32, stream);
+      return sh.K == 16 ? launch_chunk_readout<16>(q, k, v, sh, pl, sigma, ws, out, out_f32, io, stream)
+                        : launch_chunk_readout<8>(q, k, v, sh, pl, sigma, ws, out, out_f32, io, stream);
   }
 }
 

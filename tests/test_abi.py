@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.lib()
     for name in header_symbols():
         assert hasattr(lib, name), name
-    assert lib.based_abi_version() == 1
+    assert lib.based_abi_version() == 2
     for s in range(6):
         assert lib.based_status_string(s)
     assert lib.based_kernel_name(0) == b"based_segment_state_kernel"
@@ -91,3 +91,52 @@ def test_plan():
     assert g == 1 and ws == 0
     g, L, ws = plan(1, 100, 1, 8, 64, segment_len=33)
     assert L == 64 and g == 2
+
+
+def test_feature_dim():
+    lib = _lib.lib()
+    assert lib.based_feature_dim(16) == 273 and lib.based_feature_dim(8) == 73
+
+
+S_IN, Z_IN, S_OUT, Z_OUT = 0x2000000000, 0x3000000000, 0x4000000000, 0x5000000000
+
+
+def call_state(s_in=None, z_in=None, s_out=None, z_out=None, K=16, V=64, T=64, out=0x80000000, ws=None, ws_bytes=0):
+    lib = _lib.lib()
+    return lib.based_forward_state(FAKE, FAKE, FAKE, 1, T, 2, K, V, math.nan, out, 0, s_in, z_in, s_out, z_out,
+                                   ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(s_in=S_IN),                                    # state without its normaliser
+    dict(z_out=Z_OUT),                                  # normaliser out without the state out
+    dict(s_in=S_IN + 4, z_in=Z_IN),                     # misaligned
+    dict(s_out=S_OUT, z_out=Z_OUT, out=S_OUT + 64),     # out overlaps state_out
+    dict(s_in=S_IN, z_in=Z_IN, s_out=S_IN, z_out=Z_OUT),  # state_out aliases state_in
+    dict(s_out=S_OUT, z_out=S_OUT + 256),               # state_out and norm_out overlap
+])
+def test_forward_state_rejects_bad_state_arguments(kw):
+    assert call_state(**kw) == _lib.BASED_ERR_INVALID_ARGUMENT
+
+
+def test_forward_state_rejects_unsupported_shape():
+    assert call_state(s_out=S_OUT, z_out=Z_OUT, K=12) == _lib.BASED_ERR_UNSUPPORTED
+
+
+def call_decode(q=FAKE, state=S_IN, norm=Z_IN, K=16, V=64, out=0x80000000, scale=math.nan):
+    lib = _lib.lib()
+    return lib.based_decode_step(q, FAKE, FAKE, 2, 4, K, V, scale, state, norm, out, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(state=0), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(norm=Z_IN + 8), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(K=4), _lib.BASED_ERR_UNSUPPORTED),
+    (dict(V=100), _lib.BASED_ERR_UNSUPPORTED),
+    (dict(scale=math.inf), _lib.BASED_ERR_INVALID_ARGUMENT),
+    (dict(out=S_IN + 128), _lib.BASED_ERR_INVALID_ARGUMENT),  # out overlaps the state
+    (dict(norm=S_IN + 1024), _lib.BASED_ERR_INVALID_ARGUMENT),  # state and norm overlap
+])
+def test_decode_step_rejects_bad_arguments(kw, status):
+    assert call_decode(**kw) == status
