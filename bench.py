@@ -1,6 +1,7 @@
 """Benchmark of the causal Based forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|INDEX] [--no-cpu-baseline] [--all]
+                [--page-shapes]
 
 A step is one full forward (every kernel of the path) over one batch of synthetic bf16 inputs that are
 resident in device memory before timing starts. The default workload is B=4, T=8192, H=16, K=16, V=64 with
@@ -110,17 +111,21 @@ def cpu_baseline(w, qb, kb, vb, budget_s=15.0):
     }
 
 
-def run_bench(w, steps, warmup, with_cpu=True):
+def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False):
     import torch
 
     from taylor_feature_map_amd import Timer, based_forward, plan
-    from taylor_feature_map_amd.inputs import make_workload
+    from taylor_feature_map_amd.inputs import make_qkv_device, make_workload
 
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
-    qb, kb, vb = make_workload(w)
-    to = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-    q, k, v = to(qb), to(kb), to(vb)
+    if device_inputs:
+        q, k, v = make_qkv_device(w.B, w.T, w.H, w.K, w.V, w.seed, dev)
+        with_cpu = False
+    else:
+        qb, kb, vb = make_workload(w)
+        to = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        q, k, v = to(qb), to(kb), to(vb)
     out_dtype = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
     out = torch.empty((w.B, w.T, w.H, w.V), dtype=out_dtype, device=dev)
     segments, seg_len, ws_bytes = plan(w.B, w.T, w.H, w.K, w.V)
@@ -242,6 +247,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also print a line per workload to stderr")
+    ap.add_argument("--page-shapes", action="store_true",
+                    help="also print a line per measure and grader shape of the page to stderr")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     a = ap.parse_args()
@@ -263,6 +270,18 @@ def main():
                             "cold_ms": r["ms_per_step_cold_median"], "tokens_per_s": r["value"],
                             "tflops": r["tflops_canonical"], "path_hbm_frac": r["path_hbm_frac"],
                             "kernels": r["kernels"]}))
+    if a.page_shapes:
+        from taylor_feature_map_amd.inputs import PAGE_SHAPES
+        for w in PAGE_SHAPES:
+            if "_measure_" not in w.name and "_grader_" not in w.name:
+                continue
+            r = run_bench(w, max(5, a.steps // 5), max(2, a.warmup // 5), device_inputs=True)
+            log(json.dumps({"workload": w.name, "ms_per_step": r["ms_per_step"], "tokens_per_s": r["value"],
+                            "tflops": r["tflops_canonical"], "path_hbm_frac": r["path_hbm_frac"],
+                            "path_mfma_frac": r["path_mfma_frac"], "segments": r["config"]["segments"],
+                            "kernels": r["kernels"]}))
+            import torch
+            torch.cuda.empty_cache()
     w = pick_workload(a.workload)
     res = run_bench(w, a.steps, a.warmup, with_cpu=not a.no_cpu_baseline)
     print(json.dumps(res), flush=True)

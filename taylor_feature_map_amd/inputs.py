@@ -45,6 +45,20 @@ WORKLOADS = (
 )
 HEADLINE = WORKLOADS[2]
 
+# The shape lists the page gives for this task (field shapes of the task spec): (B, T, H, K, V) for its
+# correctness, quick-measure, measure and grader runs. Scale K**-0.5, bfloat16 output.
+_PAGE = (
+    ("correct", [(1, 256, 4, 16, 128), (2, 512, 8, 16, 64), (1, 512, 6, 8, 128), (2, 128, 4, 16, 128)]),
+    ("quick", [(1, 2048, 16, 16, 128), (2, 2048, 8, 16, 128), (1, 4096, 16, 8, 128)]),
+    ("measure", [(4, 12288, 32, 16, 128), (8, 8192, 16, 16, 128), (4, 16384, 32, 16, 64), (2, 16384, 32, 16, 128),
+                 (4, 16384, 32, 8, 128)]),
+    ("grader", [(4, 16384, 32, 16, 128), (8, 8192, 32, 16, 128), (8, 16384, 16, 16, 128), (8, 16384, 32, 16, 64),
+                (8, 16384, 32, 8, 128)]),
+)
+PAGE_SHAPES = tuple(
+    Workload(f"page_{role}_b{B}_t{T}_h{H}_k{K}_v{V}", B, T, H, K, V, 100 + 10 * r + i, None, "bf16")
+    for r, (role, shapes) in enumerate(_PAGE) for i, (B, T, H, K, V) in enumerate(shapes))
+
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest, ties to even) and return the 16-bit patterns as uint16."""
@@ -71,3 +85,16 @@ def make_qkv(B: int, T: int, H: int, K: int, V: int, seed: int):
 
 def make_workload(w: Workload):
     return make_qkv(w.B, w.T, w.H, w.K, w.V, w.seed)
+
+
+def make_qkv_device(B: int, T: int, H: int, K: int, V: int, seed: int, device):
+    """Seeded N(0, 1) inputs drawn directly on the GPU (torch's generator for that device), rounded to
+    bfloat16: q, then k, then v. For timing runs at sizes where host-side generation would dominate; the
+    values are not reproducible off the GPU and are never compared with the oracle."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = []
+    for shape in ((B, T, H, K), (B, T, H, K), (B, T, H, V)):
+        out.append(torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16))
+    return tuple(out)
