@@ -255,15 +255,18 @@ __device__ __forceinline__ void export_feature(const FeatRows& fr, float val, Wr
 // ----------------------------------------------------------------------------- work split
 
 // One work item (b, h, value slice, segment) runs on a workgroup of W waves over chunks of C = 32 W
-// tokens. Wave w owns the state feature tiles [T0(w), T0(w) + NT(w)) for the update, and finishes
-// the 16-token query tiles w and 2W - 1 - w of every chunk (this pairing gives every wave the same
-// causal intra-chunk work). K = 16: W = 4, tiles 3 + 3 + 2 + 2, C = 128; K = 8: W = 2, tiles 2 + 1,
-// C = 64.
+// tokens. Wave w owns the state feature tiles [T0(w), T0(w) + NT(w)) for the update, and finishes two
+// 16-token query tiles QA(w), QB(w) of every chunk. Query tile i meets i / 2 + 1 key steps inside the
+// chunk, so the pairing evens out the total work: K = 16 (W = 4, feature tiles 3 + 3 + 2 + 2, C = 128)
+// gives the waves with three feature tiles the pairs {0, 5}, {1, 4} (4 key steps each) and the others
+// {2, 7}, {3, 6} (6 each); K = 8 (W = 2, feature tiles 2 + 1, C = 64) pairs {0, 3} and {1, 2}.
 template <int K>
 struct Split {
   static constexpr int W = (K == 16) ? 4 : 2;
   static constexpr int C = 32 * W;
   __host__ __device__ static constexpr int T0(int w) { return (K == 16) ? (w < 2 ? 3 * w : 6 + 2 * (w - 2)) : 2 * w; }
+  __host__ __device__ static constexpr int QA(int w) { return w; }
+  __host__ __device__ static constexpr int QB(int w) { return (K == 16) ? (w < 2 ? 5 - w : 9 - w) : 3 - w; }
   __host__ __device__ static constexpr int NT(int w) { return (K == 16) ? (w < 2 ? 3 : 2) : (w == 0 ? 2 : 1); }
 };
 
@@ -773,7 +776,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
   using F = Feat<K>;
   using SP = Split<K>;
   constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
-  constexpr int I0 = WI, I1 = 2 * SP::W - 1 - WI;  // this wave's query tiles
+  constexpr int I0 = SP::QA(WI), I1 = SP::QB(WI);  // this wave's query tiles
   constexpr int NP = (F::NPT + 1) / 2;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -815,13 +818,19 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
     f32x4_t O[2][kVT];
     {
       float ry[2][F::NQ], hy[2][4];
+      u32x2_t qraw[2][F::NQ / 4];  // all reads first, so that their latencies overlap
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
         const u16* qrow = st.q + (16 * (ii == 0 ? I0 : I1) + c) * K;
 #pragma unroll
+        for (int kk = 0; kk < F::NQ / 4; ++kk)
+          qraw[ii][kk] = *reinterpret_cast<const u32x2_t*>(qrow + 4 * ((g + kk) & (F::NQ / 4 - 1)));
+      }
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
         for (int kk = 0; kk < F::NQ / 4; ++kk) {
-          const int base = 4 * ((g + kk) & (F::NQ / 4 - 1));
-          const u32x2_t w2 = *reinterpret_cast<const u32x2_t*>(qrow + base);
+          const u32x2_t w2 = qraw[ii][kk];
           ry[ii][4 * kk + 0] = sigma * lo_f(w2.x);
           ry[ii][4 * kk + 1] = sigma * hi_f(w2.x);
           ry[ii][4 * kk + 2] = sigma * lo_f(w2.y);
