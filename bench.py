@@ -130,7 +130,7 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False):
     out = torch.empty((w.B, w.T, w.H, w.V), dtype=out_dtype, device=dev)
     segments, seg_len, ws_bytes = plan(w.B, w.T, w.H, w.K, w.V)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    timer = Timer(max_launches=steps + 16, kernels=(Timer.READOUT,))  # events around the read-out kernel only
+    timer = Timer(max_launches=3 * steps + 16)  # events around every kernel of a step
 
     def step(t=None):
         based_forward(q, k, v, w.scale, out=out, workspace=ws, timer=t)
@@ -147,9 +147,9 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
 
-    # The same K steps again with HIP events recorded on the launch stream around the read-out kernel
-    # only (events at kernel boundaries cost several microseconds each, so the throughput above is
-    # taken without them): average duration of the dominant kernel for the roofline.
+    # The same K steps again with HIP events recorded on the launch stream around every kernel (events at
+    # kernel boundaries cost a few microseconds each, so the throughput above is taken without them): the
+    # average duration of each kernel, the dominant one giving the roofline figure.
     timer.reset()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -157,19 +157,13 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False):
         step(timer)
     torch.cuda.synchronize()
     ms_instrumented = (time.perf_counter() - t1) * 1e3 / steps
-    n_dom, ms_dom = timer.read(2)
-    dom_us = ms_dom * 1e3 / n_dom
-
-    # Per-kernel breakdown from a third pass with events around every kernel.
-    all_timer = Timer(max_launches=3 * steps + 16)
-    for _ in range(steps):
-        step(all_timer)
-    torch.cuda.synchronize()
     per_kernel = {}
     for kid in Timer.KERNELS:
-        n, ms = all_timer.read(kid)
+        n, ms = timer.read(kid)
         if n:
             per_kernel[Timer.kernel_name(kid)] = {"launches": n, "avg_us": ms * 1e3 / n}
+    n_dom, ms_dom = timer.read(Timer.READOUT)
+    dom_us = ms_dom * 1e3 / n_dom
 
     # Cold-cache steps: a 512 MiB write between steps evicts L2 and the Infinity Cache.
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
@@ -213,7 +207,7 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False):
         "tflops_canonical": flops / (ms_per_step * 1e-3) / 1e12,
         "path_hbm_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        "ms_per_step_with_readout_events": ms_instrumented,
+        "ms_per_step_with_kernel_events": ms_instrumented,
         "ms_per_step_cold_median": float(np.median(cold)) if cold else None,
         "kernels": per_kernel,
         "device": {"name": props.name, "cus": props.multi_processor_count,
