@@ -254,20 +254,31 @@ __device__ __forceinline__ void export_feature(const FeatRows& fr, float val, Wr
 
 // ----------------------------------------------------------------------------- work split
 
-// One work item (b, h, value slice, segment) runs on a workgroup of W waves over chunks of C = 32 W
-// tokens. Wave w owns the state feature tiles [T0(w), T0(w) + NT(w)) for the update, and finishes two
-// 16-token query tiles QA(w), QB(w) of every chunk. Query tile i meets i / 2 + 1 key steps inside the
-// chunk, so the pairing evens out the total work: K = 16 (W = 4, feature tiles 3 + 3 + 2 + 2, C = 128)
-// gives the waves with three feature tiles the pairs {0, 5}, {1, 4} (4 key steps each) and the others
-// {2, 7}, {3, 6} (6 each); K = 8 (W = 2, feature tiles 2 + 1, C = 64) pairs {0, 3} and {1, 2}.
+#ifndef BASED_CHUNK16
+#define BASED_CHUNK16 64
+#endif
+
+// One work item (b, h, value slice, segment) runs on a workgroup of W waves over chunks of C tokens
+// (NKS key steps of 32). Wave w owns the state feature tiles [T0(w), T0(w) + NT(w)) for the update and
+// finishes QPW of the chunk's 16-token query tiles, Q(w, 0 .. QPW - 1). Query tile i meets i / 2 + 1 key
+// steps inside the chunk, so the assignment evens out the work. K = 16: W = 4, feature tiles
+// 3 + 3 + 2 + 2, C = 64, one query tile per wave: tiles 0 and 1 (one key step) go to the waves with three
+// feature tiles, 2 and 3 (two key steps) to the others. (With C = 128 the pairs would be {0, 5}, {1, 4}
+// and {2, 7}, {3, 6}.) K = 8: W = 2, feature tiles 2 + 1, C = 64, query tile pairs {0, 3} and {1, 2}.
+// A shorter chunk means less causal work inside each chunk (a query meets C / 2 earlier keys of its
+// chunk on average) against one more state publish per C tokens.
 template <int K>
 struct Split {
   static constexpr int W = (K == 16) ? 4 : 2;
-  static constexpr int C = 32 * W;
+  static constexpr int C = (K == 16) ? BASED_CHUNK16 : 64;
+  static constexpr int NKS = C / 32;
+  static constexpr int QPW = C / 16 / W;
+  static_assert(QPW >= 1 && QPW <= 2 && QPW * 16 * W == C, "one or two query tiles per wave");
   __host__ __device__ static constexpr int T0(int w) { return (K == 16) ? (w < 2 ? 3 * w : 6 + 2 * (w - 2)) : 2 * w; }
-  __host__ __device__ static constexpr int QA(int w) { return w; }
-  __host__ __device__ static constexpr int QB(int w) { return (K == 16) ? (w < 2 ? 5 - w : 9 - w) : 3 - w; }
   __host__ __device__ static constexpr int NT(int w) { return (K == 16) ? (w < 2 ? 3 : 2) : (w == 0 ? 2 : 1); }
+  __host__ __device__ static constexpr int Q(int w, int i) {
+    return QPW == 1 ? w : (i == 0 ? w : (K == 16 ? (w < 2 ? 5 - w : 9 - w) : 3 - w));
+  }
 };
 
 // ------------------------------------------------------------------------------ LDS staging
@@ -467,15 +478,15 @@ __device__ __forceinline__ Rows make_rows(const u16* q, const u16* k, const u16*
 // tiles times KW groups of key steps. Wave w owns the feature tiles of group w / KW and the key steps
 // of group w % KW of every chunk, so the waves do equal MFMA work and each reads only its own key
 // steps' values from LDS; the KW partial sums of a feature group are added at the end of the segment.
-// K = 16: 2 x 2 (5 tiles, 2 key steps per wave); K = 8: 1 x 2 (3 tiles, 1 key step per wave).
+// K = 16: 2 x 2 (5 tiles); K = 8: 1 x 2 (3 tiles); each wave takes half the chunk's key steps.
 template <int K>
 struct StateSplit {
   static constexpr int W = Split<K>::W;
   static constexpr int KW = 2;
   static constexpr int FW = W / KW;
   static constexpr int NT = Feat<K>::NPT / FW;
-  static constexpr int KS = W / KW;  // key steps per wave and chunk
-  static_assert(NT * FW == Feat<K>::NPT && KS * KW == W, "even split");
+  static constexpr int KS = Split<K>::NKS / KW;  // key steps per wave and chunk
+  static_assert(NT * FW == Feat<K>::NPT && KS * KW == Split<K>::NKS, "even split");
 };
 
 template <int K>
@@ -776,7 +787,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
   using F = Feat<K>;
   using SP = Split<K>;
   constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
-  constexpr int I0 = SP::QA(WI), I1 = SP::QB(WI);  // this wave's query tiles
+  constexpr int QPW = SP::QPW;  // this wave's query tiles: SP::Q(WI, 0 .. QPW - 1)
   constexpr int NP = (F::NPT + 1) / 2;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -814,20 +825,20 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
     const Stage<K>& st = sm.stage[it & 1];
 
     // ---- read-out of earlier tokens through the state, transposed: O^T = S^T phi(Q)^T for this wave's
-    //      two query tiles (the bf16 state tiles are the A operand, phi(Q) the B operand).
-    f32x4_t O[2][kVT];
+    //      query tiles (the bf16 state tiles are the A operand, phi(Q) the B operand).
+    f32x4_t O[QPW][kVT];
     {
-      float ry[2][F::NQ], hy[2][4];
-      u32x2_t qraw[2][F::NQ / 4];  // all reads first, so that their latencies overlap
-#pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const u16* qrow = st.q + (16 * (ii == 0 ? I0 : I1) + c) * K;
+      float ry[QPW][F::NQ], hy[QPW][4];
+      u32x2_t qraw[QPW][F::NQ / 4];  // all reads first, so that their latencies overlap
+      constexpr_for<0, QPW>([&](auto ic) {
+        constexpr int ii = decltype(ic)::value;
+        const u16* qrow = st.q + (16 * SP::Q(WI, ii) + c) * K;
 #pragma unroll
         for (int kk = 0; kk < F::NQ / 4; ++kk)
           qraw[ii][kk] = *reinterpret_cast<const u32x2_t*>(qrow + 4 * ((g + kk) & (F::NQ / 4 - 1)));
-      }
+      });
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
+      for (int ii = 0; ii < QPW; ++ii) {
 #pragma unroll
         for (int kk = 0; kk < F::NQ / 4; ++kk) {
           const u32x2_t w2 = qraw[ii][kk];
@@ -846,7 +857,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
 #pragma unroll
         for (int vt = 0; vt < kVT; ++vt) sb[vt] = sm.sb[m][vt][lane];
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
+        for (int ii = 0; ii < QPW; ++ii) {
           u32x4_t pq;
           pq.x = pack2(F::template qval<ta, 0>(ry[ii], hy[ii], g), F::template qval<ta, 1>(ry[ii], hy[ii], g));
           pq.y = pack2(F::template qval<ta, 2>(ry[ii], hy[ii], g), F::template qval<ta, 3>(ry[ii], hy[ii], g));
@@ -858,19 +869,18 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
       });
     }
 
-    // ---- per 32-token key step: intra-chunk term (direct polynomial) for both query tiles, then fold
+    // ---- per 32-token key step: intra-chunk term (direct polynomial) for the query tiles, then fold
     //      the step into this wave's state tiles (after the last chunk the result is unused).
     const unsigned soff_out = static_cast<unsigned>(t0) * out_stride;
 #pragma unroll
-    for (int ks = 0; ks < SP::W; ++ks) {
+    for (int ks = 0; ks < SP::NKS; ++ks) {
       u32x4_t vop[kVT];
       load_value_operands<K>(st, ks, lane, vop);
-      intra_step<K, I0>(st, ks, vop, O[0], c1, c2, lane);
-      intra_step<K, I1>(st, ks, vop, O[1], c1, c2, lane);
-      if (ks == SP::W - 1) {
-        store_tile<OUT_F32>(ro, lane_off, soff_out + 16 * I0 * out_stride, O[0]);
-        store_tile<OUT_F32>(ro, lane_off, soff_out + 16 * I1 * out_stride, O[1]);
-      }
+      constexpr_for<0, QPW>([&](auto ic) {
+        constexpr int ii = decltype(ic)::value;
+        intra_step<K, SP::Q(WI, ii)>(st, ks, vop, O[ii], c1, c2, lane);
+        if (ks == SP::NKS - 1) store_tile<OUT_F32>(ro, lane_off, soff_out + 16 * SP::Q(WI, ii) * out_stride, O[ii]);
+      });
       float kx[8];
       key_column<K>(st, ks, lane, kx);
       state_update_step<K, T0, NT>(S, kx, vop, c);
