@@ -57,7 +57,7 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
   if (seg_override > 0) {
     L = (seg_override + ck - 1) / ck * ck;
   } else {
-    const int64_t waves = sh.B * sh.H * pl.nvs * (ck / 32);
+    const int64_t waves = sh.B * sh.H * pl.nvs * based::waves_per_item(sh.K);
     const int64_t g_target = (kTargetWaves + waves - 1) / waves;
     L = (sh.T + g_target - 1) / g_target;
     L = (L + ck - 1) / ck * ck;

@@ -39,9 +39,10 @@ __host__ __device__ __forceinline__ void constexpr_for(F&& f) {
 
 int state_slot_floats(int64_t K);
 
-// Tokens per chunk for feature dimension K; a work item runs on chunk_tokens(K) / 32 wavefronts and
-// segment lengths are multiples of it.
+// Tokens per chunk for feature dimension K (segment lengths are multiples of it), and wavefronts per
+// work item.
 int chunk_tokens(int64_t K);
+int waves_per_item(int64_t K);
 
 // Optional state in the page's layout, fp32: S of (B, H, P, V) and z of (B, H, P), P = 1 + K + K^2. The
 // read-out adds s_in / z_in to its starting state and writes the state after the last token to s_out /

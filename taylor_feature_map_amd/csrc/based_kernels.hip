@@ -1063,6 +1063,8 @@ int state_slot_floats(int64_t K) { return (K == 16 ? Feat<16>::NPT : Feat<8>::NP
 
 int chunk_tokens(int64_t K) { return K == 16 ? Split<16>::C : Split<8>::C; }
 
+int waves_per_item(int64_t K) { return K == 16 ? Split<16>::W : Split<8>::W; }
+
 hipError_t launch_kernel(int kernel_id, const void* q, const void* k, const void* v, const Shape& sh,
                          const Plan& pl, float sigma, float* ws, void* out, bool out_f32, const StateIO& io,
                          hipStream_t stream) {

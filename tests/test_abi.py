@@ -83,6 +83,7 @@ def test_plan():
     from taylor_feature_map_amd import plan
     g, L, ws = plan(4, 8192, 16, 16, 64)
     assert L % 32 == 0 and g == -(-8192 // L) and g * 64 >= 512
+    assert g == 8  # 64 (b, h) items x 8 segments x 4 waves = 2048 waves: two per SIMD, no more
     g, L, ws = plan(1, 65000, 16, 16, 64)
     assert (g - 1) * L < 65000 <= g * L
     g, L, ws = plan(1, 1 << 20, 1, 16, 64)
