@@ -50,14 +50,15 @@ based_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V
 
 Plan make_plan(const Shape& sh, int64_t seg_override) {
   Plan pl;
-  pl.nvs = sh.V / based::kVSlice;
-  const int64_t ck = based::chunk_tokens(sh.K);
+  pl.item_cols = based::item_columns(sh.V);
+  pl.nvs = sh.V / pl.item_cols;
+  const int64_t ck = based::chunk_tokens(sh.K, pl.item_cols);
   const int64_t t_round = (sh.T + ck - 1) / ck * ck;
   int64_t L;
   if (seg_override > 0) {
     L = (seg_override + ck - 1) / ck * ck;
   } else {
-    const int64_t waves = sh.B * sh.H * pl.nvs * based::waves_per_item(sh.K);
+    const int64_t waves = sh.B * sh.H * pl.nvs * based::waves_per_item(sh.K, pl.item_cols);
     const int64_t g_target = (kTargetWaves + waves - 1) / waves;
     L = (sh.T + g_target - 1) / g_target;
     L = (L + ck - 1) / ck * ck;
@@ -66,7 +67,7 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
   if (L > t_round) L = t_round;
   pl.seg_len = L;
   pl.segments = (sh.T + L - 1) / L;
-  pl.slot_floats = based::state_slot_floats(sh.K);
+  pl.slot_floats = based::state_slot_floats(sh.K, pl.item_cols);
   pl.scanned = pl.segments > based::kMaxSummedSegments;
   return pl;
 }

@@ -9,19 +9,18 @@
 namespace based {
 
 constexpr int kWave = 64;    // wavefront width on CDNA
-constexpr int kVSlice = 64;  // value columns per wavefront
-constexpr int kVT = 5;       // 16-column value tiles per wavefront: 4 of values, 1 of ones
 
 struct Shape {
   int64_t B, T, H, K, V;
 };
 
-// Sequence split: `segments` pieces of `seg_len` tokens (last one possibly shorter), `nvs` value
-// slices of 64 columns, `slot_floats` floats per stored segment state sum. With `scanned` set, the
-// stored sums are turned into prefix sums by a scan kernel before the read-out; otherwise every
-// read-out adds up the sums of its predecessors itself.
+// Sequence split: `segments` pieces of `seg_len` tokens (last one possibly shorter); work items of
+// `item_cols` value columns (64, or 128 when V is a multiple of 128), `nvs` of them per (b, h);
+// `slot_floats` floats per stored segment state sum. With `scanned` set, the stored sums are turned into
+// prefix sums by a scan kernel before the read-out; otherwise every read-out adds up the sums of its
+// predecessors itself.
 struct Plan {
-  int64_t segments, seg_len, nvs, slot_floats;
+  int64_t segments, seg_len, nvs, item_cols, slot_floats;
   bool scanned;
 };
 
@@ -37,12 +36,12 @@ __host__ __device__ __forceinline__ void constexpr_for(F&& f) {
   }
 }
 
-int state_slot_floats(int64_t K);
-
-// Tokens per chunk for feature dimension K (segment lengths are multiples of it), and wavefronts per
-// work item.
-int chunk_tokens(int64_t K);
-int waves_per_item(int64_t K);
+// Value columns per work item for V; floats per segment state sum, tokens per chunk (segment lengths are
+// multiples of it) and wavefronts per work item for feature dimension K and `item_cols` columns.
+int item_columns(int64_t V);
+int state_slot_floats(int64_t K, int64_t item_cols);
+int chunk_tokens(int64_t K, int64_t item_cols);
+int waves_per_item(int64_t K, int64_t item_cols);
 
 // Optional state in the page's layout, fp32: S of (B, H, P, V) and z of (B, H, P), P = 1 + K + K^2. The
 // read-out adds s_in / z_in to its starting state and writes the state after the last token to s_out /

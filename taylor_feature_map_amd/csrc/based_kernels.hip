@@ -258,24 +258,46 @@ __device__ __forceinline__ void export_feature(const FeatRows& fr, float val, Wr
 #define BASED_CHUNK16 64
 #endif
 
-// One work item (b, h, value slice, segment) runs on a workgroup of W waves over chunks of C tokens
+// Compile-time configuration of a work item: feature dimension K and VS value columns (64, or 128 when V
+// is a multiple of 128), plus the ones tile that carries the normaliser: NVT = VS / 16 + 1 value tiles,
+// the ones tile last.
+template <int K_, int VS_>
+struct Cfg {
+  static constexpr int K = K_;
+  static constexpr int VS = VS_;
+  static constexpr int NVV = VS / 16;  // value tiles
+  static constexpr int NVT = NVV + 1;  // value tiles and the ones tile
+  static constexpr int ONES = NVV;     // index of the ones tile
+};
+
+// One work item (b, h, value columns, segment) runs on a workgroup of W waves over chunks of C tokens
 // (NKS key steps of 32). Wave w owns the state feature tiles [T0(w), T0(w) + NT(w)) for the update and
 // finishes QPW of the chunk's 16-token query tiles, Q(w, 0 .. QPW - 1). Query tile i meets i / 2 + 1 key
-// steps inside the chunk, so the assignment evens out the work. K = 16: W = 4, feature tiles
-// 3 + 3 + 2 + 2, C = 64, one query tile per wave: tiles 0 and 1 (one key step) go to the waves with three
-// feature tiles, 2 and 3 (two key steps) to the others. (With C = 128 the pairs would be {0, 5}, {1, 4}
-// and {2, 7}, {3, 6}.) K = 8: W = 2, feature tiles 2 + 1, C = 64, query tile pairs {0, 3} and {1, 2}.
-// A shorter chunk means less causal work inside each chunk (a query meets C / 2 earlier keys of its
-// chunk on average) against one more state publish per C tokens.
-template <int K>
+// steps inside the chunk, so the assignment evens out the work: the waves with more feature tiles take
+// the query tiles with fewer earlier keys in the chunk.
+//   K = 16, 64 columns:  W = 4, C = 64, feature tiles 3 + 3 + 2 + 2, one query tile per wave.
+//   K = 16, 128 columns: W = 8, C = 128, feature tiles 2 + 2 + 1 x 6, one query tile per wave.
+//   K = 8, 64 columns:   W = 2, C = 64, feature tiles 2 + 1, query tile pairs {0, 3} and {1, 2}.
+//   K = 8, 128 columns:  W = 4, C = 64, feature tiles 1 + 1 + 1 + 0, one query tile per wave.
+// (With C = 128 and 64 columns, K = 16 would pair {0, 5}, {1, 4} and {2, 7}, {3, 6}.) A shorter chunk
+// means less causal work inside each chunk (a query meets C / 2 earlier keys of its chunk on average)
+// against one more state publish per C tokens; 128 columns share phi, the scores and the ones tile
+// between twice as many outputs.
+template <class Cf>
 struct Split {
-  static constexpr int W = (K == 16) ? 4 : 2;
-  static constexpr int C = (K == 16) ? BASED_CHUNK16 : 64;
+  static constexpr int K = Cf::K;
+  static constexpr bool WIDE = Cf::VS == 128;
+  static constexpr int W = K == 16 ? (WIDE ? 8 : 4) : (WIDE ? 4 : 2);
+  static constexpr int C = K == 16 ? (WIDE ? 128 : BASED_CHUNK16) : 64;
   static constexpr int NKS = C / 32;
   static constexpr int QPW = C / 16 / W;
   static_assert(QPW >= 1 && QPW <= 2 && QPW * 16 * W == C, "one or two query tiles per wave");
-  __host__ __device__ static constexpr int T0(int w) { return (K == 16) ? (w < 2 ? 3 * w : 6 + 2 * (w - 2)) : 2 * w; }
-  __host__ __device__ static constexpr int NT(int w) { return (K == 16) ? (w < 2 ? 3 : 2) : (w == 0 ? 2 : 1); }
+  __host__ __device__ static constexpr int T0(int w) {
+    return K == 16 ? (WIDE ? (w < 2 ? 2 * w : w + 2) : (w < 2 ? 3 * w : 6 + 2 * (w - 2))) : (WIDE ? w : 2 * w);
+  }
+  __host__ __device__ static constexpr int NT(int w) {
+    return K == 16 ? (WIDE ? (w < 2 ? 2 : 1) : (w < 2 ? 3 : 2)) : (WIDE ? (w < 3 ? 1 : 0) : (w == 0 ? 2 : 1));
+  }
   __host__ __device__ static constexpr int Q(int w, int i) {
     return QPW == 1 ? w : (i == 0 ? w : (K == 16 ? (w < 2 ? 5 - w : 9 - w) : 3 - w));
   }
@@ -283,40 +305,42 @@ struct Split {
 
 // ------------------------------------------------------------------------------ LDS staging
 
-// One chunk of one (b, h, value slice), natural row layout: q[C][K], k[C][K], and v in blocks of 8
-// tokens x 64 columns where the 16-byte unit `oct` (columns 8 oct .. 8 oct + 7) of token t is stored at
-// position oct ^ (t % 8).
-template <int K>
+// One chunk of one work item, natural row layout: q[C][K], k[C][K], and v[C][VS] where the 16-byte unit
+// `oct` (columns 8 oct .. 8 oct + 7) of token t is stored at position oct ^ (t % 8).
+template <class Cf>
 struct __align__(16) Stage {
-  static constexpr int C = Split<K>::C;
-  u16 q[C * K];
-  u16 k[C * K];
-  u16 v[C * 64];
+  static constexpr int C = Split<Cf>::C;
+  u16 q[C * Cf::K];
+  u16 k[C * Cf::K];
+  u16 v[C * Cf::VS];
 };
 
+template <int VS>
 __device__ __forceinline__ int v_index(int tok, int col) {
-  return (tok >> 3) * 512 + (tok & 7) * 64 + (((col >> 3) ^ (tok & 7)) << 3) + (col & 7);
+  return tok * VS + (((col >> 3) ^ (tok & 7)) << 3) + (col & 7);
 }
 
-// The 16-byte units of one chunk: NQK q units, NQK k units, then 8 C value units. Unit u lands at u16
-// offset 8 u of its LDS region. Global reads go through buffer resources whose range ends at token T, so
-// units of tokens >= T read as zero; such tokens only ever meet zero Taylor weights or an update whose
+// The 16-byte units of one chunk: NQK q units, NQK k units, then C VS / 8 value units. Unit u lands at
+// u16 offset 8 u of its LDS region. Global reads go through buffer resources whose range ends at token T,
+// so units of tokens >= T read as zero; such tokens only ever meet zero Taylor weights or an update whose
 // result is discarded.
-template <int K>
+template <class Cf>
 struct Units {
-  static constexpr int C = Split<K>::C;
+  static constexpr int K = Cf::K;
+  static constexpr int C = Split<Cf>::C;
+  static constexpr int UPR = Cf::VS / 8;  // value units per token row
   static constexpr int NQK = C * K / 8;
-  static constexpr int NV = C * 8;
+  static constexpr int NV = C * UPR;
   static constexpr int NU = 2 * NQK + NV;
   static constexpr int PER_Q = K / 8;  // units per token row of q or k
   // Byte offset of q/k unit u relative to the chunk's first token.
   __device__ static __forceinline__ unsigned qk_off(int u, unsigned stride_bytes) {
     return (u / PER_Q) * stride_bytes + (u % PER_Q) * 16;
   }
-  // Byte offset of value unit f relative to the chunk's first token.
+  // Byte offset of value unit f (LDS position f % UPR of token f / UPR) relative to the chunk's first token.
   __device__ static __forceinline__ unsigned v_off(int f, unsigned stride_bytes) {
-    const int blk = f >> 6, l = f & 63, row = l >> 3;
-    return (blk * 8 + row) * stride_bytes + (((l & 7) ^ row) << 4);
+    const int tok = f / UPR, pos = f % UPR;
+    return tok * stride_bytes + ((pos ^ (tok & 7)) << 4);
   }
 };
 
@@ -340,10 +364,10 @@ struct Rows {
 // Chunk loader: the units of q (if WITH_Q), k and v spread over all threads of the workgroup, one
 // chunk ahead of use, through registers. Every region is a multiple of 64 units long, so the region of
 // each of wave WI's loads is known at compile time (no divergent branches around the loads).
-template <int K, bool WITH_Q, int WI>
+template <class Cf, bool WITH_Q, int WI>
 struct Prefetch {
-  using U = Units<K>;
-  static constexpr int NTH = Split<K>::W * kWave;
+  using U = Units<Cf>;
+  static constexpr int NTH = Split<Cf>::W * kWave;
   static constexpr int FIRST = WITH_Q ? 0 : U::NQK;  // q units are skipped without q
   static constexpr int PER = (U::NU - FIRST + NTH - 1) / NTH;
   static_assert(U::NQK % kWave == 0 && U::NV % kWave == 0, "regions must be whole waves");
@@ -375,7 +399,7 @@ struct Prefetch {
       else if constexpr (reg == 2) r[i] = buf_load16(rw.v, off[i], sv);
     });
   }
-  __device__ __forceinline__ void store(Stage<K>& st, int lane) const {
+  __device__ __forceinline__ void store(Stage<Cf>& st, int lane) const {
     constexpr_for<0, PER>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       constexpr int reg = region(i);
@@ -389,19 +413,20 @@ struct Prefetch {
 
 // B operand of value tile vt for contraction step ks (tokens 32 ks .. 32 ks + 31): column m <-> value
 // column 16 vt + m; slot e <-> token 32 ks + 16(e/4) + 4g + e%4.
-template <int K>
-__device__ __forceinline__ u32x4_t value_operand(const Stage<K>& st, int ks, int vt, int lane) {
+template <class Cf>
+__device__ __forceinline__ u32x4_t value_operand(const Stage<Cf>& st, int ks, int vt, int lane) {
   const int g = lane >> 4, r = lane & 15;
   const int col = 16 * vt + 4 * (r & 3);
   const int tok = 32 * ks + 4 * g + (r >> 2);
-  const u32x2_t a = lds_tr16(st.v + v_index(tok, col));
-  const u32x2_t b = lds_tr16(st.v + v_index(tok + 16, col));
+  const u32x2_t a = lds_tr16(st.v + v_index<Cf::VS>(tok, col));
+  const u32x2_t b = lds_tr16(st.v + v_index<Cf::VS>(tok + 16, col));
   return u32x4_t{a.x, a.y, b.x, b.y};
 }
 
 // Key feature c (K = 8: c % 8) of the lane's 8 token slots of contraction step ks, as floats.
-template <int K>
-__device__ __forceinline__ void key_column(const Stage<K>& st, int ks, int lane, float* kx) {
+template <class Cf>
+__device__ __forceinline__ void key_column(const Stage<Cf>& st, int ks, int lane, float* kx) {
+  constexpr int K = Cf::K;
   const int g = lane >> 4, r = lane & 15;
   const int f4 = (K == 16) ? 4 * (r & 3) : 4 * (r & 1);
   const int tok = 32 * ks + 4 * g + (r >> 2);
@@ -411,9 +436,10 @@ __device__ __forceinline__ void key_column(const Stage<K>& st, int ks, int lane,
   kx[4] = lo_f(b.x); kx[5] = hi_f(b.x); kx[6] = lo_f(b.y); kx[7] = hi_f(b.y);
 }
 
-// S[tiles T0 .. T0 + NT) (features x [64 values | ones]) += phi(K)^T [V | 1] over one 32-token step.
-template <int K, int T0, int NT, typename SA>
-__device__ __forceinline__ void state_update_step(SA& S, const float* kx, const u32x4_t (&vop)[kVT], int c) {
+// S[tiles T0 .. T0 + NT) (features x [VS values | ones]) += phi(K)^T [V | 1] over one 32-token step.
+template <class Cf, int T0, int NT, typename SA>
+__device__ __forceinline__ void state_update_step(SA& S, const float* kx, const u32x4_t (&vop)[Cf::NVT], int c) {
+  constexpr int K = Cf::K;
   constexpr_for<0, NT>([&](auto lc) {
     constexpr int lt = decltype(lc)::value;
     constexpr int t = T0 + lt;
@@ -423,24 +449,27 @@ __device__ __forceinline__ void state_update_step(SA& S, const float* kx, const 
     a.z = pack2(Feat<K>::template kval<t>(kx[4], c), Feat<K>::template kval<t>(kx[5], c));
     a.w = pack2(Feat<K>::template kval<t>(kx[6], c), Feat<K>::template kval<t>(kx[7], c));
 #pragma unroll
-    for (int vt = 0; vt < kVT; ++vt) S[lt][vt] = mfma32(a, vop[vt], S[lt][vt]);
+    for (int vt = 0; vt < Cf::NVT; ++vt) S[lt][vt] = mfma32(a, vop[vt], S[lt][vt]);
   });
 }
 
-template <int K>
-__device__ __forceinline__ void load_value_operands(const Stage<K>& st, int ks, int lane, u32x4_t (&vop)[kVT]) {
+template <class Cf>
+__device__ __forceinline__ void load_value_operands(const Stage<Cf>& st, int ks, int lane, u32x4_t (&vop)[Cf::NVT]) {
 #pragma unroll
-  for (int vt = 0; vt < 4; ++vt) vop[vt] = value_operand<K>(st, ks, vt, lane);
-  vop[4] = u32x4_t{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
+  for (int vt = 0; vt < Cf::NVV; ++vt) vop[vt] = value_operand<Cf>(st, ks, vt, lane);
+  vop[Cf::ONES] = u32x4_t{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 }
 
-// Register-native layout of one segment state sum in the workspace, 16 bytes (the four rows r) per lane
-// and tile: the value tiles as [tile][value tile][lane][r], then the ones tile, whose 16 columns are
-// equal, as [tile][lane group][r].
-__device__ __forceinline__ int64_t state_offset(int t, int vt, int lane) { return ((t * 4 + vt) * kWave + lane) * 4; }
-template <int K>
+// Register-native layout of one segment state sum of a work item with VS value columns in the workspace,
+// 16 bytes (the four rows r) per lane and tile: the value tiles as [tile][value tile][lane][r], then the
+// ones tile, whose 16 columns are equal, as [tile][lane group][r].
+template <int VS>
+__device__ __forceinline__ int64_t state_offset(int t, int vt, int lane) {
+  return ((t * (VS / 16) + vt) * kWave + lane) * 4;
+}
+template <int K, int VS>
 __device__ __forceinline__ int64_t ones_offset(int t, int g) {
-  return Feat<K>::NPT * 16 * kWave + (t * 4 + g) * 4;
+  return Feat<K>::NPT * (VS / 16) * 4 * kWave + (t * 4 + g) * 4;
 }
 
 struct ItemCoords {
@@ -458,11 +487,12 @@ __device__ __forceinline__ ItemCoords decode_item(int64_t item, int64_t H, int64
   return ic;
 }
 
-template <int K>
+// ic.vs counts work items of VS columns.
+template <int K, int VS>
 __device__ __forceinline__ Rows make_rows(const u16* q, const u16* k, const u16* v, const Shape& sh,
                                           const ItemCoords& ic) {
   const int64_t bh_qk = (ic.b * sh.T * sh.H + ic.h) * K;
-  const int64_t bh_v = (ic.b * sh.T * sh.H + ic.h) * sh.V + ic.vs * kVSlice;
+  const int64_t bh_v = (ic.b * sh.T * sh.H + ic.h) * sh.V + ic.vs * VS;
   Rows rw;
   rw.qk_stride = static_cast<unsigned>(sh.H * K * 2);
   rw.v_stride = static_cast<unsigned>(sh.H * sh.V * 2);
@@ -478,59 +508,63 @@ __device__ __forceinline__ Rows make_rows(const u16* q, const u16* k, const u16*
 // tiles times KW groups of key steps. Wave w owns the feature tiles of group w / KW and the key steps
 // of group w % KW of every chunk, so the waves do equal MFMA work and each reads only its own key
 // steps' values from LDS; the KW partial sums of a feature group are added at the end of the segment.
-// K = 16: 2 x 2 (5 tiles); K = 8: 1 x 2 (3 tiles); each wave takes half the chunk's key steps.
-template <int K>
+// The state kernel always works on 64 value columns (SC); with 128-column read-out items it writes each
+// half into the item's slot. K = 16: 2 x 2 (5 tiles); K = 8: 1 x 2 (3 tiles); each wave takes half the
+// chunk's key steps.
+template <class Cf>
 struct StateSplit {
-  static constexpr int W = Split<K>::W;
+  static constexpr int W = Split<Cf>::W;
   static constexpr int KW = 2;
   static constexpr int FW = W / KW;
-  static constexpr int NT = Feat<K>::NPT / FW;
-  static constexpr int KS = Split<K>::NKS / KW;  // key steps per wave and chunk
-  static_assert(NT * FW == Feat<K>::NPT && KS * KW == Split<K>::NKS, "even split");
+  static constexpr int NT = Feat<Cf::K>::NPT / FW;
+  static constexpr int KS = Split<Cf>::NKS / KW;  // key steps per wave and chunk
+  static_assert(NT * FW == Feat<Cf::K>::NPT && KS * KW == Split<Cf>::NKS, "even split");
 };
 
-template <int K>
+template <class Cf>
 struct __align__(16) StateSmem {
   union {
-    Stage<K> stage[2];
-    f32x4_t red[StateSplit<K>::FW][StateSplit<K>::NT][kVT][kWave];  // partial sums of key-step group 1
+    Stage<Cf> stage[2];
+    f32x4_t red[StateSplit<Cf>::FW][StateSplit<Cf>::NT][Cf::NVT][kWave];  // partial sums of key-step group 1
   };
 };
 
-template <int K, int WI>
-__device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows& rw, int64_t T, int64_t t_begin,
-                                                   int64_t t_end, float* __restrict__ dst) {
-  using SP = Split<K>;
-  using SS = StateSplit<K>;
+// half: which 64 columns of the slot's IVS columns this work item covers (the ones tile goes with half 0).
+template <class SC, int IVS, int WI>
+__device__ __forceinline__ void segment_state_body(StateSmem<SC>& sm, const Rows& rw, int64_t T, int64_t t_begin,
+                                                   int64_t t_end, int half, float* __restrict__ dst) {
+  using SP = Split<SC>;
+  using SS = StateSplit<SC>;
+  constexpr int K = SC::K;
   constexpr int FG = WI / SS::KW, KG = WI % SS::KW;
   constexpr int T0 = FG * SS::NT, NT = SS::NT;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int c = lane & 15;
-  f32x4_t S[NT][kVT];
+  f32x4_t S[NT][SC::NVT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int vt = 0; vt < kVT; ++vt) S[t][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int vt = 0; vt < SC::NVT; ++vt) S[t][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // As in the read-out: chunk c + 1 is loaded at the top of iteration c and staged at its end.
-  Prefetch<K, false, WI> pf;
+  Prefetch<SC, false, WI> pf;
   pf.init(rw, lane);
   pf.load(rw, t_begin);
   pf.store(sm.stage[0], lane);
   int it = 0;
   for (int64_t t0 = t_begin; t0 < t_end; t0 += SP::C, ++it) {
-    const Stage<K>& st = sm.stage[it & 1];
+    const Stage<SC>& st = sm.stage[it & 1];
     pf.load(rw, t0 + SP::C < t_end ? t0 + SP::C : T);  // past the range after the last chunk: no traffic
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < SS::KS; ++j) {
       const int ks = KG * SS::KS + j;
-      u32x4_t vop[kVT];
-      load_value_operands<K>(st, ks, lane, vop);
+      u32x4_t vop[SC::NVT];
+      load_value_operands<SC>(st, ks, lane, vop);
       float kx[8];
-      key_column<K>(st, ks, lane, kx);
-      state_update_step<K, T0, NT>(S, kx, vop, c);
+      key_column<SC>(st, ks, lane, kx);
+      state_update_step<SC, T0, NT>(S, kx, vop, c);
     }
     pf.store(sm.stage[(it + 1) & 1], lane);  // read in iteration c - 1, finished before this iteration's barrier
   }
@@ -539,43 +573,50 @@ __device__ __forceinline__ void segment_state_body(StateSmem<K>& sm, const Rows&
 #pragma unroll
     for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-      for (int vt = 0; vt < kVT; ++vt) sm.red[FG][lt][vt][lane] = S[lt][vt];
+      for (int vt = 0; vt < SC::NVT; ++vt) sm.red[FG][lt][vt][lane] = S[lt][vt];
   }
   __syncthreads();
   if constexpr (KG == 0) {
 #pragma unroll
     for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-      for (int vt = 0; vt < kVT; ++vt) S[lt][vt] += sm.red[FG][lt][vt][lane];
+      for (int vt = 0; vt < SC::NVT; ++vt) S[lt][vt] += sm.red[FG][lt][vt][lane];
 #pragma unroll
     for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-      for (int vt = 0; vt < 4; ++vt) *reinterpret_cast<f32x4_t*>(dst + state_offset(T0 + lt, vt, lane)) = S[lt][vt];
-    if (c == 0) {
+      for (int vt = 0; vt < SC::NVV; ++vt)
+        *reinterpret_cast<f32x4_t*>(dst + state_offset<IVS>(T0 + lt, SC::NVV * half + vt, lane)) = S[lt][vt];
+    if (half == 0 && c == 0) {
 #pragma unroll
       for (int lt = 0; lt < NT; ++lt)
-        *reinterpret_cast<f32x4_t*>(dst + ones_offset<K>(T0 + lt, lane >> 4)) = S[lt][4];
+        *reinterpret_cast<f32x4_t*>(dst + ones_offset<K, IVS>(T0 + lt, lane >> 4)) = S[lt][SC::ONES];
     }
   }
 }
 
-template <int K>
-__global__ __launch_bounds__(Split<K>::W * kWave) void based_segment_state_kernel(
+// Work items of 64 columns (pl.nvs64 per (b, h)); the slot belongs to the read-out item of IVS columns that
+// contains them.
+template <int K, int IVS>
+__global__ __launch_bounds__((Split<Cfg<K, 64>>::W * kWave)) void based_segment_state_kernel(
     const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float* __restrict__ ws) {
+  using SC = Cfg<K, 64>;
+  constexpr int HALVES = IVS / 64;
   const int64_t item = item_of_block();
-  const int64_t items = sh.B * sh.H * pl.nvs * (pl.segments - 1);
+  const int64_t nvs64 = pl.nvs * HALVES;
+  const int64_t items = sh.B * sh.H * nvs64 * (pl.segments - 1);
   if (item >= items) return;
-  const ItemCoords ic = decode_item(item, sh.H, pl.nvs, pl.segments - 1);
-  __shared__ StateSmem<K> sm;
-  const Rows rw = make_rows<K>(k, k, v, sh, ic);
+  const ItemCoords ic = decode_item(item, sh.H, nvs64, pl.segments - 1);
+  __shared__ StateSmem<SC> sm;
+  const Rows rw = make_rows<K, 64>(k, k, v, sh, ic);
   const int64_t t_begin = ic.g * pl.seg_len;
   const int64_t t_end = t_begin + pl.seg_len;  // full segment: only the last one can be short
-  const int64_t bhv = (ic.b * sh.H + ic.h) * pl.nvs + ic.vs;
+  const int64_t bhv = (ic.b * sh.H + ic.h) * pl.nvs + ic.vs / HALVES;
+  const int half = static_cast<int>(ic.vs % HALVES);
   float* dst = ws + (bhv * (pl.segments - 1) + ic.g) * pl.slot_floats;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr_for<0, Split<K>::W>([&](auto wc) {
+  constexpr_for<0, Split<SC>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
-    if (w == WI) segment_state_body<K, WI>(sm, rw, sh.T, t_begin, t_end, dst);
+    if (w == WI) segment_state_body<SC, IVS, WI>(sm, rw, sh.T, t_begin, t_end, half, dst);
   });
 }
 
@@ -614,22 +655,21 @@ __global__ __launch_bounds__(256) void based_segment_scan_kernel(float* __restri
 
 // ------------------------------------------------------------------- kernel 2: chunked read-out
 
-constexpr int kMaxPairs = 5;  // tile pairs of the read-out contraction (K = 16)
-
-template <int K>
+template <class Cf>
 struct __align__(16) ReadoutSmem {
-  Stage<K> stage[2];                  // chunk c in stage[c % 2]; chunk c + 1 is staged during chunk c
-  u32x4_t sb[kMaxPairs][kVT][kWave];  // bf16 state: tile pair m, value tile, lane (D register layout)
+  static constexpr int NP = (Feat<Cf::K>::NPT + 1) / 2;  // tile pairs of the read-out contraction
+  Stage<Cf> stage[2];                  // chunk c in stage[c % 2]; chunk c + 1 is staged during chunk c
+  u32x4_t sb[NP][Cf::NVT][kWave];      // bf16 state: tile pair m, value tile, lane (D register layout)
 };
 
 // bf16 copy of this wave's state tiles into the shared tile-pair layout.
-template <int K, int T0, int NT, typename SA>
-__device__ __forceinline__ void publish_state(ReadoutSmem<K>& sm, const SA& S, int lane) {
+template <class Cf, int T0, int NT, typename SA>
+__device__ __forceinline__ void publish_state(ReadoutSmem<Cf>& sm, const SA& S, int lane) {
 #pragma unroll
   for (int lt = 0; lt < NT; ++lt) {
     const int t = T0 + lt;
 #pragma unroll
-    for (int vt = 0; vt < kVT; ++vt) {
+    for (int vt = 0; vt < Cf::NVT; ++vt) {
       u32x2_t* d = reinterpret_cast<u32x2_t*>(&sm.sb[t >> 1][vt][lane]) + (t & 1);
       *d = u32x2_t{pack2(S[lt][vt][0], S[lt][vt][1]), pack2(S[lt][vt][2], S[lt][vt][3])};
     }
@@ -639,9 +679,10 @@ __device__ __forceinline__ void publish_state(ReadoutSmem<K>& sm, const SA& S, i
 // Intra-chunk contribution of key step ks (key tokens 32 ks .. 32 ks + 31) to 16-token query tile II:
 // scores K Q^T on the 16x16x16 MFMA, Taylor weights, then the transposed product [V | 1]^T A^T, so
 // that the output tile comes out with the token along the lanes.
-template <int K, int II>
-__device__ __forceinline__ void intra_step(const Stage<K>& st, int ks, const u32x4_t (&vop)[kVT], f32x4_t (&O)[kVT],
-                                           float c1, float c2, int lane) {
+template <class Cf, int II>
+__device__ __forceinline__ void intra_step(const Stage<Cf>& st, int ks, const u32x4_t (&vop)[Cf::NVT],
+                                           f32x4_t (&O)[Cf::NVT], float c1, float c2, int lane) {
+  constexpr int K = Cf::K;
   if (2 * ks > II) return;
   const int c = lane & 15, g = lane >> 4;
   u32x2_t qb = {0u, 0u};
@@ -676,7 +717,7 @@ __device__ __forceinline__ void intra_step(const Stage<K>& st, int ks, const u32
   }
   const u32x4_t aop = {pack2(w[0], w[1]), pack2(w[2], w[3]), pack2(w[4], w[5]), pack2(w[6], w[7])};
 #pragma unroll
-  for (int vt = 0; vt < kVT; ++vt) O[vt] = mfma32(vop[vt], aop, O[vt]);
+  for (int vt = 0; vt < Cf::NVT; ++vt) O[vt] = mfma32(vop[vt], aop, O[vt]);
 }
 
 // o = num / (den + 1e-6) for one 16-token query tile held transposed: lane (c, g) has token c of the
@@ -684,12 +725,12 @@ __device__ __forceinline__ void intra_step(const Stage<K>& st, int ks, const u32
 // 16-byte (fp32) store per lane; the ones tile holds den in all four rows. voff is the lane's byte
 // offset of (token c, column 4 g); the tile's first token goes into the scalar offset. Rows past the end
 // of the sequence fall outside the output buffer range and are dropped.
-template <bool OUT_F32>
+template <class Cf, bool OUT_F32>
 __device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned voff, unsigned soff,
-                                           const f32x4_t (&O)[kVT]) {
-  const float inv = __builtin_amdgcn_rcpf(O[4][0] + 1e-6f);
+                                           const f32x4_t (&O)[Cf::NVT]) {
+  const float inv = __builtin_amdgcn_rcpf(O[Cf::ONES][0] + 1e-6f);
 #pragma unroll
-  for (int vt = 0; vt < 4; ++vt) {
+  for (int vt = 0; vt < Cf::NVV; ++vt) {
     if constexpr (OUT_F32) {
       const f32x4_t o = O[vt] * inv;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, voff, soff + 64 * vt, 0);
@@ -702,31 +743,32 @@ __device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned v
 
 // The state at the start of a segment: the sum, in segment order, of the state sums of the `n_src`
 // earlier segments stored at src, src + slot_floats, ...
-template <int K, int T0, int NT, typename SA>
+template <class Cf, int T0, int NT, typename SA>
 __device__ __forceinline__ void initial_state(SA& S, const float* __restrict__ src, int64_t n_src, int64_t slot_floats,
                                               int lane) {
   const int g = lane >> 4;
 #pragma unroll
   for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-    for (int vt = 0; vt < kVT; ++vt) S[lt][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int vt = 0; vt < Cf::NVT; ++vt) S[lt][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int64_t i = 0; i < n_src; ++i) {
     const float* s = src + i * slot_floats;
-    f32x4_t x[NT][kVT];
+    f32x4_t x[NT > 0 ? NT : 1][Cf::NVT];
 #pragma unroll
     for (int lt = 0; lt < NT; ++lt) {
 #pragma unroll
-      for (int vt = 0; vt < 4; ++vt) x[lt][vt] = *reinterpret_cast<const f32x4_t*>(s + state_offset(T0 + lt, vt, lane));
-      x[lt][4] = *reinterpret_cast<const f32x4_t*>(s + ones_offset<K>(T0 + lt, g));
+      for (int vt = 0; vt < Cf::NVV; ++vt)
+        x[lt][vt] = *reinterpret_cast<const f32x4_t*>(s + state_offset<Cf::VS>(T0 + lt, vt, lane));
+      x[lt][Cf::ONES] = *reinterpret_cast<const f32x4_t*>(s + ones_offset<Cf::K, Cf::VS>(T0 + lt, g));
     }
 #pragma unroll
     for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-      for (int vt = 0; vt < kVT; ++vt) S[lt][vt] += x[lt][vt];
+      for (int vt = 0; vt < Cf::NVT; ++vt) S[lt][vt] += x[lt][vt];
   }
 }
 
-// A state in the page's layout for one (b, h) and value slice: entry (row r, slice column j) of S at
+// A state in the page's layout for one (b, h) and work item: entry (row r, item column j) of S at
 // s[r * V + j], of z at z[r]. Import when s_in is set, export (of the state after the last token) when
 // s_out is set; write_z selects the one value slice that writes z.
 struct StateView {
@@ -738,8 +780,9 @@ struct StateView {
   bool write_z;
 };
 
-template <int K, int T0, int NT, typename SA>
+template <class Cf, int T0, int NT, typename SA>
 __device__ __forceinline__ void import_state(SA& S, const StateView& sv, int lane) {
+  constexpr int K = Cf::K;
   const int c = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int lt = 0; lt < NT; ++lt) {
@@ -747,19 +790,20 @@ __device__ __forceinline__ void import_state(SA& S, const StateView& sv, int lan
     for (int r = 0; r < 4; ++r) {
       const FeatRows fr = feat_rows<K>(T0 + lt, 4 * g + r);
 #pragma unroll
-      for (int vt = 0; vt < 4; ++vt) {
+      for (int vt = 0; vt < Cf::NVV; ++vt) {
         const float* col = sv.s_in + 16 * vt + c;
         S[lt][vt][r] += import_feature<K>(fr, [&](int row) { return col[row * sv.V]; });
       }
-      S[lt][4][r] += import_feature<K>(fr, [&](int row) { return sv.z_in[row]; });
+      S[lt][Cf::ONES][r] += import_feature<K>(fr, [&](int row) { return sv.z_in[row]; });
     }
   }
 }
 
 // The padding tokens of a ragged last chunk (k = v = 0, so phi(k) = [1, 0, ...]) added `n_pad` to the
 // constant feature of z and nothing else; the exported z leaves them out.
-template <int K, int T0, int NT, typename SA>
+template <class Cf, int T0, int NT, typename SA>
 __device__ __forceinline__ void export_state(const SA& S, const StateView& sv, float n_pad, int lane) {
+  constexpr int K = Cf::K;
   const int c = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int lt = 0; lt < NT; ++lt) {
@@ -767,25 +811,27 @@ __device__ __forceinline__ void export_state(const SA& S, const StateView& sv, f
     for (int r = 0; r < 4; ++r) {
       const FeatRows fr = feat_rows<K>(T0 + lt, 4 * g + r);
 #pragma unroll
-      for (int vt = 0; vt < 4; ++vt) {
+      for (int vt = 0; vt < Cf::NVV; ++vt) {
         float* col = sv.s_out + 16 * vt + c;
         export_feature<K>(fr, S[lt][vt][r], [&](int row, float x) { col[row * sv.V] = x; });
       }
       if (sv.write_z && c == 0) {
-        const float zv = fr.kind == kFeatConst ? S[lt][4][r] - n_pad : S[lt][4][r];
+        const float zv = fr.kind == kFeatConst ? S[lt][Cf::ONES][r] - n_pad : S[lt][Cf::ONES][r];
         export_feature<K>(fr, zv, [&](int row, float x) { sv.z_out[row] = x; });
       }
     }
   }
 }
 
-template <int K, int WI, bool OUT_F32>
-__device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw, __amdgpu_buffer_rsrc_t ro,
+template <class Cf, int WI, bool OUT_F32>
+__device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw, __amdgpu_buffer_rsrc_t ro,
                                              unsigned out_stride, int64_t T, int64_t t_begin, int64_t t_end,
                                              float c1, float c2, float sigma, const float* __restrict__ src,
                                              int64_t n_src, int64_t slot_floats, const StateView& sv) {
+  constexpr int K = Cf::K;
+  constexpr int NVT = Cf::NVT;
   using F = Feat<K>;
-  using SP = Split<K>;
+  using SP = Split<Cf>;
   constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
   constexpr int QPW = SP::QPW;  // this wave's query tiles: SP::Q(WI, 0 .. QPW - 1)
   constexpr int NP = (F::NPT + 1) / 2;
@@ -796,14 +842,14 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
   constexpr unsigned kOutBytes = OUT_F32 ? 4 : 2;
   const unsigned lane_off = c * out_stride + 4 * g * kOutBytes;
 
-  f32x4_t S[NT][kVT];
-  initial_state<K, T0, NT>(S, src, n_src, slot_floats, lane);
-  if (sv.s_in) import_state<K, T0, NT>(S, sv, lane);
-  publish_state<K, T0, NT>(sm, S, lane);
-  if constexpr (F::NPT % 2 == 1 && T0 + NT == F::NPT) {
+  f32x4_t S[NT > 0 ? NT : 1][NVT];
+  initial_state<Cf, T0, NT>(S, src, n_src, slot_floats, lane);
+  if (sv.s_in) import_state<Cf, T0, NT>(S, sv, lane);
+  publish_state<Cf, T0, NT>(sm, S, lane);
+  if constexpr (F::NPT % 2 == 1 && T0 + NT == F::NPT && NT > 0) {
     // The last tile pair is half empty: its second half stays zero for the whole kernel.
 #pragma unroll
-    for (int vt = 0; vt < kVT; ++vt)
+    for (int vt = 0; vt < NVT; ++vt)
       reinterpret_cast<u32x2_t*>(&sm.sb[F::NPT >> 1][vt][lane])[1] = u32x2_t{0u, 0u};
   }
 
@@ -812,7 +858,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
   // no load result is pending across the loop's back edge (which would make the memory-counter wait
   // at the top cover this chunk's output stores too). Loads past the segment read the next segment's
   // (or out-of-range, zero) rows and are never used.
-  Prefetch<K, true, WI> pf;
+  Prefetch<Cf, true, WI> pf;
   pf.init(rw, lane);
   pf.load(rw, t_begin);
   pf.store(sm.stage[0], lane);
@@ -822,11 +868,11 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
     // zeros without touching memory.
     pf.load(rw, t0 + SP::C < t_end ? t0 + SP::C : T);
     __syncthreads();  // this chunk's inputs and the bf16 state of earlier chunks are in LDS
-    const Stage<K>& st = sm.stage[it & 1];
+    const Stage<Cf>& st = sm.stage[it & 1];
 
     // ---- read-out of earlier tokens through the state, transposed: O^T = S^T phi(Q)^T for this wave's
     //      query tiles (the bf16 state tiles are the A operand, phi(Q) the B operand).
-    f32x4_t O[QPW][kVT];
+    f32x4_t O[QPW][NVT];
     {
       float ry[QPW][F::NQ], hy[QPW][4];
       u32x2_t qraw[QPW][F::NQ / 4];  // all reads first, so that their latencies overlap
@@ -853,9 +899,9 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
       constexpr_for<0, NP>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         constexpr int ta = 2 * m, tb = 2 * m + 1;
-        u32x4_t sb[kVT];
+        u32x4_t sb[NVT];
 #pragma unroll
-        for (int vt = 0; vt < kVT; ++vt) sb[vt] = sm.sb[m][vt][lane];
+        for (int vt = 0; vt < NVT; ++vt) sb[vt] = sm.sb[m][vt][lane];
 #pragma unroll
         for (int ii = 0; ii < QPW; ++ii) {
           u32x4_t pq;
@@ -864,7 +910,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
           pq.z = pack2(F::template qval<tb, 0>(ry[ii], hy[ii], g), F::template qval<tb, 1>(ry[ii], hy[ii], g));
           pq.w = pack2(F::template qval<tb, 2>(ry[ii], hy[ii], g), F::template qval<tb, 3>(ry[ii], hy[ii], g));
 #pragma unroll
-          for (int vt = 0; vt < kVT; ++vt) O[ii][vt] = mfma32(sb[vt], pq, m == 0 ? zero4 : O[ii][vt]);
+          for (int vt = 0; vt < NVT; ++vt) O[ii][vt] = mfma32(sb[vt], pq, m == 0 ? zero4 : O[ii][vt]);
         }
       });
     }
@@ -874,38 +920,42 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<K>& sm, const Rows& rw,
     const unsigned soff_out = static_cast<unsigned>(t0) * out_stride;
 #pragma unroll
     for (int ks = 0; ks < SP::NKS; ++ks) {
-      u32x4_t vop[kVT];
-      load_value_operands<K>(st, ks, lane, vop);
+      u32x4_t vop[NVT];
+      load_value_operands<Cf>(st, ks, lane, vop);
       constexpr_for<0, QPW>([&](auto ic) {
         constexpr int ii = decltype(ic)::value;
-        intra_step<K, SP::Q(WI, ii)>(st, ks, vop, O[ii], c1, c2, lane);
-        if (ks == SP::NKS - 1) store_tile<OUT_F32>(ro, lane_off, soff_out + 16 * SP::Q(WI, ii) * out_stride, O[ii]);
+        intra_step<Cf, SP::Q(WI, ii)>(st, ks, vop, O[ii], c1, c2, lane);
+        if (ks == SP::NKS - 1)
+          store_tile<Cf, OUT_F32>(ro, lane_off, soff_out + 16 * SP::Q(WI, ii) * out_stride, O[ii]);
       });
-      float kx[8];
-      key_column<K>(st, ks, lane, kx);
-      state_update_step<K, T0, NT>(S, kx, vop, c);
+      if constexpr (NT > 0) {
+        float kx[8];
+        key_column<Cf>(st, ks, lane, kx);
+        state_update_step<Cf, T0, NT>(S, kx, vop, c);
+      }
     }
     __syncthreads();  // every wave is done with the old bf16 state
-    publish_state<K, T0, NT>(sm, S, lane);
+    publish_state<Cf, T0, NT>(sm, S, lane);
     pf.store(sm.stage[(it + 1) & 1], lane);  // that buffer's chunk c - 1 was finished before the last barrier
   }
   if (sv.s_out && t_end == T) {
     const int64_t n = t_end - t_begin;
-    export_state<K, T0, NT>(S, sv, static_cast<float>((n + SP::C - 1) / SP::C * SP::C - n), lane);
+    export_state<Cf, T0, NT>(S, sv, static_cast<float>((n + SP::C - 1) / SP::C * SP::C - n), lane);
   }
 }
 
-template <int K, bool OUT_F32>
-__global__ __launch_bounds__(Split<K>::W * kWave) void based_chunk_readout_kernel(
+template <int K, int VS, bool OUT_F32>
+__global__ __launch_bounds__((Split<Cfg<K, VS>>::W * kWave)) void based_chunk_readout_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float c1,
     float c2, float sigma, const float* __restrict__ ws, void* __restrict__ out, StateIO io) {
+  using Cf = Cfg<K, VS>;
   const int64_t item = item_of_block();
   const int64_t items = sh.B * sh.H * pl.nvs * pl.segments;
   if (item >= items) return;
   const ItemCoords ic = decode_item(item, sh.H, pl.nvs, pl.segments);
-  __shared__ ReadoutSmem<K> sm;
-  const Rows rw = make_rows<K>(q, k, v, sh, ic);
-  const int64_t bh_v = (ic.b * sh.T * sh.H + ic.h) * sh.V + ic.vs * kVSlice;
+  __shared__ ReadoutSmem<Cf> sm;
+  const Rows rw = make_rows<K, VS>(q, k, v, sh, ic);
+  const int64_t bh_v = (ic.b * sh.T * sh.H + ic.h) * sh.V + ic.vs * VS;
   const unsigned out_stride = static_cast<unsigned>(sh.H * sh.V * (OUT_F32 ? 4 : 2));
   const __amdgpu_buffer_rsrc_t ro =
       make_rsrc(static_cast<char*>(out) + bh_v * (OUT_F32 ? 4 : 2), sh.T, out_stride);
@@ -923,18 +973,18 @@ __global__ __launch_bounds__(Split<K>::W * kWave) void based_chunk_readout_kerne
   StateView sv;
   const int64_t P = 1 + K + K * K;
   const int64_t bh = ic.b * sh.H + ic.h;
-  sv.s_in = io.s_in ? io.s_in + bh * P * sh.V + ic.vs * kVSlice : nullptr;
+  sv.s_in = io.s_in ? io.s_in + bh * P * sh.V + ic.vs * VS : nullptr;
   sv.z_in = io.z_in ? io.z_in + bh * P : nullptr;
-  sv.s_out = io.s_out ? io.s_out + bh * P * sh.V + ic.vs * kVSlice : nullptr;
+  sv.s_out = io.s_out ? io.s_out + bh * P * sh.V + ic.vs * VS : nullptr;
   sv.z_out = io.z_out ? io.z_out + bh * P : nullptr;
   sv.V = sh.V;
   sv.write_z = ic.vs == 0;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr_for<0, Split<K>::W>([&](auto wc) {
+  constexpr_for<0, Split<Cf>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
     if (w == WI)
-      readout_body<K, WI, OUT_F32>(sm, rw, ro, out_stride, sh.T, t_begin, t_end, c1, c2, sigma, src, n_src,
-                                   pl.slot_floats, sv);
+      readout_body<Cf, WI, OUT_F32>(sm, rw, ro, out_stride, sh.T, t_begin, t_end, c1, c2, sigma, src, n_src,
+                                    pl.slot_floats, sv);
   });
 }
 
@@ -1006,13 +1056,13 @@ __global__ __launch_bounds__(256) void based_decode_step_kernel(const u16* __res
 
 // ------------------------------------------------------------------------------- host launchers
 
-template <int K>
+template <int K, int VS>
 hipError_t launch_segment_state(const void* k, const void* v, const Shape& sh, const Plan& pl, float* ws,
                                 hipStream_t stream) {
-  const int64_t items = sh.B * sh.H * pl.nvs * (pl.segments - 1);
+  const int64_t items = sh.B * sh.H * (pl.nvs * VS / 64) * (pl.segments - 1);
   const int64_t blocks = (items + 7) / 8 * 8;
-  hipLaunchKernelGGL(based_segment_state_kernel<K>, dim3(static_cast<unsigned>(blocks)),
-                     dim3(Split<K>::W * kWave), 0, stream, static_cast<const u16*>(k),
+  hipLaunchKernelGGL((based_segment_state_kernel<K, VS>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(Split<Cfg<K, 64>>::W * kWave), 0, stream, static_cast<const u16*>(k),
                      static_cast<const u16*>(v), sh, pl, ws);
   return hipGetLastError();
 }
@@ -1026,7 +1076,7 @@ hipError_t launch_segment_scan(const Shape& sh, const Plan& pl, float* ws, hipSt
   return hipGetLastError();
 }
 
-template <int K>
+template <int K, int VS>
 hipError_t launch_chunk_readout(const void* q, const void* k, const void* v, const Shape& sh, const Plan& pl,
                                 float sigma, const float* ws, void* out, bool out_f32, const StateIO& io,
                                 hipStream_t stream) {
@@ -1034,14 +1084,13 @@ hipError_t launch_chunk_readout(const void* q, const void* k, const void* v, con
   const int64_t blocks = (items + 7) / 8 * 8;
   const float c1 = sigma;
   const float c2 = 0.5f * sigma * sigma;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(Split<Cfg<K, VS>>::W * kWave);
   if (out_f32) {
-    hipLaunchKernelGGL((based_chunk_readout_kernel<K, true>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(Split<K>::W * kWave), 0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                       static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out, io);
+    hipLaunchKernelGGL((based_chunk_readout_kernel<K, VS, true>), grid, block, 0, stream, static_cast<const u16*>(q),
+                       static_cast<const u16*>(k), static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out, io);
   } else {
-    hipLaunchKernelGGL((based_chunk_readout_kernel<K, false>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(Split<K>::W * kWave), 0, stream, static_cast<const u16*>(q), static_cast<const u16*>(k),
-                       static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out, io);
+    hipLaunchKernelGGL((based_chunk_readout_kernel<K, VS, false>), grid, block, 0, stream, static_cast<const u16*>(q),
+                       static_cast<const u16*>(k), static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out, io);
   }
   return hipGetLastError();
 }
@@ -1059,24 +1108,40 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, int64
   return hipGetLastError();
 }
 
-int state_slot_floats(int64_t K) { return (K == 16 ? Feat<16>::NPT : Feat<8>::NPT) * (16 * kWave + 16); }
+int item_columns(int64_t V) { return V % 128 == 0 ? 128 : 64; }
 
-int chunk_tokens(int64_t K) { return K == 16 ? Split<16>::C : Split<8>::C; }
+int state_slot_floats(int64_t K, int64_t VS) {
+  return (K == 16 ? Feat<16>::NPT : Feat<8>::NPT) * (static_cast<int>(VS / 16) * 4 * kWave + 16);
+}
 
-int waves_per_item(int64_t K) { return K == 16 ? Split<16>::W : Split<8>::W; }
+int chunk_tokens(int64_t K, int64_t VS) {
+  return K == 16 ? (VS == 128 ? Split<Cfg<16, 128>>::C : Split<Cfg<16, 64>>::C)
+                 : (VS == 128 ? Split<Cfg<8, 128>>::C : Split<Cfg<8, 64>>::C);
+}
+
+int waves_per_item(int64_t K, int64_t VS) {
+  return K == 16 ? (VS == 128 ? Split<Cfg<16, 128>>::W : Split<Cfg<16, 64>>::W)
+                 : (VS == 128 ? Split<Cfg<8, 128>>::W : Split<Cfg<8, 64>>::W);
+}
 
 hipError_t launch_kernel(int kernel_id, const void* q, const void* k, const void* v, const Shape& sh,
                          const Plan& pl, float sigma, float* ws, void* out, bool out_f32, const StateIO& io,
                          hipStream_t stream) {
+  const bool wide = pl.item_cols == 128;
   switch (kernel_id) {
     case 0:
-      return sh.K == 16 ? launch_segment_state<16>(k, v, sh, pl, ws, stream)
-                        : launch_segment_state<8>(k, v, sh, pl, ws, stream);
+      if (sh.K == 16) return wide ? launch_segment_state<16, 128>(k, v, sh, pl, ws, stream)
+                                  : launch_segment_state<16, 64>(k, v, sh, pl, ws, stream);
+      return wide ? launch_segment_state<8, 128>(k, v, sh, pl, ws, stream)
+                  : launch_segment_state<8, 64>(k, v, sh, pl, ws, stream);
     case 1:
       return launch_segment_scan(sh, pl, ws, stream);
     default:
-      return sh.K == 16 ? launch_chunk_readout<16>(q, k, v, sh, pl, sigma, ws, out, out_f32, io, stream)
-                        : launch_chunk_readout<8>(q, k, v, sh, pl, sigma, ws, out, out_f32, io, stream);
+      if (sh.K == 16)
+        return wide ? launch_chunk_readout<16, 128>(q, k, v, sh, pl, sigma, ws, out, out_f32, io, stream)
+                    : launch_chunk_readout<16, 64>(q, k, v, sh, pl, sigma, ws, out, out_f32, io, stream);
+      return wide ? launch_chunk_readout<8, 128>(q, k, v, sh, pl, sigma, ws, out, out_f32, io, stream)
+                  : launch_chunk_readout<8, 64>(q, k, v, sh, pl, sigma, ws, out, out_f32, io, stream);
   }
 }
 
