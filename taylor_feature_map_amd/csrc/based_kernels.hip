@@ -114,9 +114,18 @@ __device__ __forceinline__ int64_t item_of_block() {
 template <int K>
 struct Feat;
 
+// Query side, for the lane's token: u[m] = q[(4g + m) mod NQ'] (the raw values, rotated per lane group;
+// NQ' = K), and for the lane's own four rows r: a[r] = scale^2 u[r], h[r] = a[r] / 2, l[r] = scale u[r].
+// The scale factors sit on the lane's own row only, so a product needs one multiply.
+struct QSide {
+  const float* u;
+  const float* a;
+  const float* h;
+  const float* l;
+};
+
 // K = 16. k side: lane column c holds x = k[c] for one token; tile T returns that lane's feature.
-// q side: ry[m] = y[(4g + m) mod 16] with y = scale * q (rotated per lane group), hy[r] = ry[r] / 2;
-// feature (T, n = 4g + R) is returned for slot R.
+// q side: feature (T, n = 4g + R) is returned for slot R.
 template <>
 struct Feat<16> {
   static constexpr int NPT = 10;
@@ -135,16 +144,16 @@ struct Feat<16> {
     }
   }
   template <int T, int R>
-  __device__ static __forceinline__ float qval(const float* ry, const float* hy, int g) {
+  __device__ static __forceinline__ float qval(const QSide& y, int g) {
     if constexpr (T == 0) {
-      return ry[R] * hy[R];
+      return y.h[R] * y.u[R];
     } else if constexpr (T <= 7) {
-      return ry[R] * ry[(R - T) & 15];
+      return y.a[R] * y.u[(R - T) & 15];
     } else if constexpr (T == 8) {
-      const float p = ry[R] * ry[(R - 8) & 15];
+      const float p = y.a[R] * y.u[(R - 8) & 15];
       return g < 2 ? p : ((g == 2 && R == 0) ? 1.0f : 0.0f);
     } else if constexpr (T == 9) {
-      return ry[R];
+      return y.l[R];
     } else {
       return 0.0f;
     }
@@ -154,7 +163,7 @@ struct Feat<16> {
 // K = 8: the 16-lane row holds the 8 features twice (lane c has feature c % 8); half h = c / 8.
 // Tiles: 0 = {h0: diagonal, h1: distance 1}, 1 = {h0: distance 2, h1: distance 3},
 //        2 = {h0: distance 4 on features 0..3, constant on feature 4, h1: linear}; 45 of 48 used.
-// q side: ry[m] = y[(4 (g & 1) + m) mod 8].
+// q side: u[m] = q[(4 (g & 1) + m) mod 8].
 template <>
 struct Feat<8> {
   static constexpr int NPT = 3;
@@ -176,15 +185,15 @@ struct Feat<8> {
     }
   }
   template <int T, int R>
-  __device__ static __forceinline__ float qval(const float* ry, const float* hy, int g) {
+  __device__ static __forceinline__ float qval(const QSide& y, int g) {
     const bool h0 = g < 2;
     if constexpr (T == 0) {
-      return h0 ? ry[R] * hy[R] : ry[R] * ry[(R - 1) & 7];
+      return h0 ? y.h[R] * y.u[R] : y.a[R] * y.u[(R - 1) & 7];
     } else if constexpr (T == 1) {
-      return h0 ? ry[R] * ry[(R - 2) & 7] : ry[R] * ry[(R - 3) & 7];
+      return y.a[R] * y.u[(R - (h0 ? 2 : 3)) & 7];
     } else if constexpr (T == 2) {
-      const float p = ry[R] * ry[(R - 4) & 7];
-      return h0 ? ((g & 1) == 0 ? p : (R == 0 ? 1.0f : 0.0f)) : ry[R];
+      const float p = y.a[R] * y.u[(R - 4) & 7];
+      return h0 ? ((g & 1) == 0 ? p : (R == 0 ? 1.0f : 0.0f)) : y.l[R];
     } else {
       return 0.0f;
     }
@@ -623,11 +632,12 @@ __global__ __launch_bounds__((Split<Cfg<K, 64>>::W * kWave)) void based_segment_
 // ------------------------------------------------------------- kernel 1: prefix over segments
 
 // Used when there are too many segments for each read-out to add up its predecessors' sums: in place,
-// slot s of every (b, h, value slice) becomes the sum of the segment sums 0..s. Slots are read in batches
-// ahead of the running sum so that the loads of a batch do not wait for the stores of the previous one.
+// slot s of every (b, h, work item columns) becomes the sum of the segment sums 0..s. Slots are read in
+// batches ahead of the running sum so that the loads of a batch do not wait for the stores of the previous
+// one; with up to 32 slots every load is issued before the first add.
 __global__ __launch_bounds__(256) void based_segment_scan_kernel(float* __restrict__ ws, int64_t n_bhv,
                                                                  int64_t slots, int64_t slot_floats) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= n_bhv * slot_floats) return;
   const int64_t bhv = idx / slot_floats;
@@ -655,22 +665,27 @@ __global__ __launch_bounds__(256) void based_segment_scan_kernel(float* __restri
 
 // ------------------------------------------------------------------- kernel 2: chunked read-out
 
+// With 64-column items the bf16 state is double-buffered (chunk c reads buffer c % 2, the state after
+// chunk c is published into the other one), which leaves one barrier per chunk. With 128 columns one
+// buffer is kept (with K = 16 a second one would not fit next to two 128-token stages) and the waves meet
+// once more before the state is overwritten.
 template <class Cf>
 struct __align__(16) ReadoutSmem {
   static constexpr int NP = (Feat<Cf::K>::NPT + 1) / 2;  // tile pairs of the read-out contraction
+  static constexpr int NSB = Cf::VS == 64 ? 2 : 1;
   Stage<Cf> stage[2];                  // chunk c in stage[c % 2]; chunk c + 1 is staged during chunk c
-  u32x4_t sb[NP][Cf::NVT][kWave];      // bf16 state: tile pair m, value tile, lane (D register layout)
+  u32x4_t sb[NSB][NP][Cf::NVT][kWave];  // bf16 state: buffer, tile pair m, value tile, lane (D layout)
 };
 
-// bf16 copy of this wave's state tiles into the shared tile-pair layout.
+// bf16 copy of this wave's state tiles into the shared tile-pair layout of buffer b.
 template <class Cf, int T0, int NT, typename SA>
-__device__ __forceinline__ void publish_state(ReadoutSmem<Cf>& sm, const SA& S, int lane) {
+__device__ __forceinline__ void publish_state(ReadoutSmem<Cf>& sm, int b, const SA& S, int lane) {
 #pragma unroll
   for (int lt = 0; lt < NT; ++lt) {
     const int t = T0 + lt;
 #pragma unroll
     for (int vt = 0; vt < Cf::NVT; ++vt) {
-      u32x2_t* d = reinterpret_cast<u32x2_t*>(&sm.sb[t >> 1][vt][lane]) + (t & 1);
+      u32x2_t* d = reinterpret_cast<u32x2_t*>(&sm.sb[b][t >> 1][vt][lane]) + (t & 1);
       *d = u32x2_t{pack2(S[lt][vt][0], S[lt][vt][1]), pack2(S[lt][vt][2], S[lt][vt][3])};
     }
   }
@@ -751,9 +766,9 @@ __device__ __forceinline__ void initial_state(SA& S, const float* __restrict__ s
   for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
     for (int vt = 0; vt < Cf::NVT; ++vt) S[lt][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int64_t i = 0; i < n_src; ++i) {
+  // Two slots are loaded before either is added (the additions keep the segment order).
+  auto load = [&](f32x4_t (&x)[NT > 0 ? NT : 1][Cf::NVT], int64_t i) {
     const float* s = src + i * slot_floats;
-    f32x4_t x[NT > 0 ? NT : 1][Cf::NVT];
 #pragma unroll
     for (int lt = 0; lt < NT; ++lt) {
 #pragma unroll
@@ -761,10 +776,25 @@ __device__ __forceinline__ void initial_state(SA& S, const float* __restrict__ s
         x[lt][vt] = *reinterpret_cast<const f32x4_t*>(s + state_offset<Cf::VS>(T0 + lt, vt, lane));
       x[lt][Cf::ONES] = *reinterpret_cast<const f32x4_t*>(s + ones_offset<Cf::K, Cf::VS>(T0 + lt, g));
     }
+  };
+  auto add = [&](const f32x4_t (&x)[NT > 0 ? NT : 1][Cf::NVT]) {
 #pragma unroll
     for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
       for (int vt = 0; vt < Cf::NVT; ++vt) S[lt][vt] += x[lt][vt];
+  };
+  int64_t i = 0;
+  for (; i + 1 < n_src; i += 2) {
+    f32x4_t x0[NT > 0 ? NT : 1][Cf::NVT], x1[NT > 0 ? NT : 1][Cf::NVT];
+    load(x0, i);
+    load(x1, i + 1);
+    add(x0);
+    add(x1);
+  }
+  if (i < n_src) {
+    f32x4_t x0[NT > 0 ? NT : 1][Cf::NVT];
+    load(x0, i);
+    add(x0);
   }
 }
 
@@ -839,18 +869,22 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw
   const int lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const float sigma2 = 2.0f * c2;  // scale^2 (c2 = scale^2 / 2)
   constexpr unsigned kOutBytes = OUT_F32 ? 4 : 2;
   const unsigned lane_off = c * out_stride + 4 * g * kOutBytes;
 
   f32x4_t S[NT > 0 ? NT : 1][NVT];
   initial_state<Cf, T0, NT>(S, src, n_src, slot_floats, lane);
   if (sv.s_in) import_state<Cf, T0, NT>(S, sv, lane);
-  publish_state<Cf, T0, NT>(sm, S, lane);
+  constexpr int NSB = ReadoutSmem<Cf>::NSB;
+  publish_state<Cf, T0, NT>(sm, 0, S, lane);
   if constexpr (F::NPT % 2 == 1 && T0 + NT == F::NPT && NT > 0) {
     // The last tile pair is half empty: its second half stays zero for the whole kernel.
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt)
-      reinterpret_cast<u32x2_t*>(&sm.sb[F::NPT >> 1][vt][lane])[1] = u32x2_t{0u, 0u};
+    for (int b = 0; b < NSB; ++b)
+#pragma unroll
+      for (int vt = 0; vt < NVT; ++vt)
+        reinterpret_cast<u32x2_t*>(&sm.sb[b][F::NPT >> 1][vt][lane])[1] = u32x2_t{0u, 0u};
   }
 
   // Chunk c is read from stage[c % 2]. Chunk c + 1 is loaded into registers at the top of iteration c
@@ -874,7 +908,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw
     //      query tiles (the bf16 state tiles are the A operand, phi(Q) the B operand).
     f32x4_t O[QPW][NVT];
     {
-      float ry[QPW][F::NQ], hy[QPW][4];
+      float qu[QPW][F::NQ], qa[QPW][4], qh[QPW][4], ql[QPW][4];
       u32x2_t qraw[QPW][F::NQ / 4];  // all reads first, so that their latencies overlap
       constexpr_for<0, QPW>([&](auto ic) {
         constexpr int ii = decltype(ic)::value;
@@ -888,27 +922,35 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw
 #pragma unroll
         for (int kk = 0; kk < F::NQ / 4; ++kk) {
           const u32x2_t w2 = qraw[ii][kk];
-          ry[ii][4 * kk + 0] = sigma * lo_f(w2.x);
-          ry[ii][4 * kk + 1] = sigma * hi_f(w2.x);
-          ry[ii][4 * kk + 2] = sigma * lo_f(w2.y);
-          ry[ii][4 * kk + 3] = sigma * hi_f(w2.y);
+          qu[ii][4 * kk + 0] = lo_f(w2.x);
+          qu[ii][4 * kk + 1] = hi_f(w2.x);
+          qu[ii][4 * kk + 2] = lo_f(w2.y);
+          qu[ii][4 * kk + 3] = hi_f(w2.y);
         }
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hy[ii][r] = 0.5f * ry[ii][r];
+      for (int ii = 0; ii < QPW; ++ii) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          qa[ii][r] = sigma2 * qu[ii][r];
+          qh[ii][r] = c2 * qu[ii][r];
+          ql[ii][r] = sigma * qu[ii][r];
+        }
       }
       constexpr_for<0, NP>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         constexpr int ta = 2 * m, tb = 2 * m + 1;
         u32x4_t sb[NVT];
 #pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) sb[vt] = sm.sb[m][vt][lane];
+        for (int vt = 0; vt < NVT; ++vt) sb[vt] = sm.sb[NSB == 2 ? (it & 1) : 0][m][vt][lane];
 #pragma unroll
         for (int ii = 0; ii < QPW; ++ii) {
+          const QSide y{qu[ii], qa[ii], qh[ii], ql[ii]};
           u32x4_t pq;
-          pq.x = pack2(F::template qval<ta, 0>(ry[ii], hy[ii], g), F::template qval<ta, 1>(ry[ii], hy[ii], g));
-          pq.y = pack2(F::template qval<ta, 2>(ry[ii], hy[ii], g), F::template qval<ta, 3>(ry[ii], hy[ii], g));
-          pq.z = pack2(F::template qval<tb, 0>(ry[ii], hy[ii], g), F::template qval<tb, 1>(ry[ii], hy[ii], g));
-          pq.w = pack2(F::template qval<tb, 2>(ry[ii], hy[ii], g), F::template qval<tb, 3>(ry[ii], hy[ii], g));
+          pq.x = pack2(F::template qval<ta, 0>(y, g), F::template qval<ta, 1>(y, g));
+          pq.y = pack2(F::template qval<ta, 2>(y, g), F::template qval<ta, 3>(y, g));
+          pq.z = pack2(F::template qval<tb, 0>(y, g), F::template qval<tb, 1>(y, g));
+          pq.w = pack2(F::template qval<tb, 2>(y, g), F::template qval<tb, 3>(y, g));
 #pragma unroll
           for (int vt = 0; vt < NVT; ++vt) O[ii][vt] = mfma32(sb[vt], pq, m == 0 ? zero4 : O[ii][vt]);
         }
@@ -934,8 +976,10 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw
         state_update_step<Cf, T0, NT>(S, kx, vop, c);
       }
     }
-    __syncthreads();  // every wave is done with the old bf16 state
-    publish_state<Cf, T0, NT>(sm, S, lane);
+    // The state after this chunk goes into the buffer that chunk c - 1 read (every wave finished that
+    // chunk before this chunk's barrier); with a single buffer the waves first wait for each other.
+    if constexpr (NSB == 1) __syncthreads();
+    publish_state<Cf, T0, NT>(sm, NSB == 2 ? ((it + 1) & 1) : 0, S, lane);
     pf.store(sm.stage[(it + 1) & 1], lane);  // that buffer's chunk c - 1 was finished before the last barrier
   }
   if (sv.s_out && t_end == T) {
