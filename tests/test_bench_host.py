@@ -1,0 +1,53 @@
+"""Host-side pieces of bench.py: the work model, the one-GPU guard and the oracle baseline leg.
+
+The FLOP model is the page's canonical count (page "Write a fast Based (Taylor linear attention) forward
+kernel", field flops_src, with C = 64); the byte model counts q, k, v read once and o written once. The
+expected numbers below are those two formulas evaluated by hand for the benchmark shapes.
+"""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from taylor_feature_map_amd.inputs import Workload, make_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_work_model_benchmark_shapes():
+    # (B, T, H, K, V, output bytes) -> canonical FLOPs, algorithmic bytes
+    cases = [
+        ((1, 512, 2, 8, 64, 4), 28_573_696, 425_984),
+        ((4, 8192, 16, 16, 64, 2), 42_010_148_864, 167_772_160),
+        ((8, 4096, 16, 16, 128, 2), 82_946_555_904, 301_989_888),
+        ((1, 65000, 16, 16, 64, 2), 83_333_120_000, 332_800_000),
+    ]
+    for (B, T, H, K, V, ob), flops, nbytes in cases:
+        assert bench.canonical_flops(B, T, H, K, V) == flops
+        assert bench.algorithmic_bytes(B, T, H, K, V, ob) == nbytes
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_figure_only_for_its_workload():
+    assert bench.measured_traffic("b2_t2048_h8_k16_v64") is None
+
+
+def test_oracle_baseline_leg():
+    w = Workload(name="tiny", B=1, T=96, H=2, K=8, V=16, seed=5, scale=None, out_dtype="bf16")
+    qb, kb, vb = make_workload(w)
+    r = bench.cpu_baseline(w, qb, kb, vb, budget_s=0.2)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s"
+    assert r["cores"] >= 1
+    assert r["seconds"] >= 0.2 - 1e-9
+    assert np.isfinite(r["value"]) and r["value"] > 0
+    # at least one (b, h) sequence, and more than one pass over the two pairs in 0.2 s of oracle time
+    assert "(b,h) sequences of T=96" in r["sample"]
