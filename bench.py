@@ -1,11 +1,13 @@
 """Benchmark of the causal Based forward on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|INDEX] [--no-cpu-baseline] [--all]
-                [--page-shapes]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--workload NAME|INDEX]
+                [--no-cpu-baseline] [--all] [--page-shapes]
 
 A step is one full forward (every kernel of the path) over one batch of synthetic bf16 inputs that are
-resident in device memory before timing starts. The default workload is B=4, T=8192, H=16, K=16, V=64 with
-bf16 output. Prints one JSON line on stdout; diagnostics go to stderr.
+resident in device memory before timing starts. Before the W warm-up steps, untimed steps run back to back
+for at least MS milliseconds (default 300) so that the GPU clocks have settled; then exactly K steps are
+timed. The default workload is B=4, T=8192, H=16, K=16, V=64 with bf16 output. Prints one JSON line on
+stdout; diagnostics go to stderr.
 
 Work model: canonical FLOPs B*H*T*(4*P*V + 2*64*(K+V)), P = 1+K+K*K (field flops_src of the page "Write a
 fast Based (Taylor linear attention) forward kernel"); algorithmic bytes = q, k, v read once + o written
@@ -115,7 +117,7 @@ def cpu_baseline(w, qb, kb, vb, budget_s=10.0):
     }
 
 
-def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False):
+def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3):
     import torch
 
     from taylor_feature_map_amd import Timer, based_forward, plan
@@ -139,6 +141,16 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False):
     def step(t=None):
         based_forward(q, k, v, w.scale, out=out, workspace=ws, timer=t)
 
+    # Settle: untimed back-to-back steps for at least settle_s seconds before the warm-up steps. The GPU
+    # needs tens of milliseconds of continuous work to reach its loaded clocks (the first ~30 ms of a
+    # burst run ~15% slower), far more than a few warm-up steps of this size take.
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < settle_s:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        n_settle += 20
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -196,6 +208,7 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False):
         "n_gpus": 1,
         "steps": steps,
         "warmup": warmup,
+        "settle_steps": n_settle,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -242,6 +255,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed back-to-back steps for at least this long before the warm-up steps")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also print a line per workload to stderr")
@@ -263,7 +278,7 @@ def main():
     if a.all:
         from taylor_feature_map_amd.inputs import WORKLOADS
         for w in WORKLOADS:
-            r = run_bench(w, a.steps, a.warmup, with_cpu=False)
+            r = run_bench(w, a.steps, a.warmup, with_cpu=False, settle_s=a.settle_ms / 1e3)
             log(json.dumps({"workload": w.name, "ms_per_step": r["ms_per_step"],
                             "cold_ms": r["ms_per_step_cold_median"], "tokens_per_s": r["value"],
                             "tflops": r["tflops_canonical"], "path_hbm_frac": r["path_hbm_frac"],
@@ -273,7 +288,8 @@ def main():
         for w in PAGE_SHAPES:
             if "_measure_" not in w.name and "_grader_" not in w.name:
                 continue
-            r = run_bench(w, max(5, a.steps // 5), max(2, a.warmup // 5), device_inputs=True)
+            r = run_bench(w, max(5, a.steps // 5), max(2, a.warmup // 5), device_inputs=True,
+                          settle_s=a.settle_ms / 1e3)
             log(json.dumps({"workload": w.name, "ms_per_step": r["ms_per_step"], "tokens_per_s": r["value"],
                             "tflops": r["tflops_canonical"], "path_hbm_frac": r["path_hbm_frac"],
                             "path_mfma_frac": r["path_mfma_frac"], "segments": r["config"]["segments"],
@@ -281,7 +297,7 @@ def main():
             import torch
             torch.cuda.empty_cache()
     w = pick_workload(a.workload)
-    res = run_bench(w, a.steps, a.warmup, with_cpu=not a.no_cpu_baseline)
+    res = run_bench(w, a.steps, a.warmup, with_cpu=not a.no_cpu_baseline, settle_s=a.settle_ms / 1e3)
     print(json.dumps(res), flush=True)
 
 

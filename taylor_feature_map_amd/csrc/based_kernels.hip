@@ -988,6 +988,22 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw
   }
 }
 
+// Segment order of the read-out blocks when each work item adds up its predecessors' sums (the start-up
+// of segment g reads g sums). Blocks are dealt to the CUs of an XCD in order, one per CU first, so the two
+// workgroups sharing a CU are the j-th and (j + n/2)-th of the XCD's n blocks: d = n / (2 H NVS) segment
+// positions apart. Positions are taken in runs of 2d as [G-1-dk .. G-d-dk, dk .. dk+d-1], which puts
+// segment g next to segment G-1-g: one of the two starts computing at once while the other reads, and the
+// long start-up goes to the older workgroup, which the scheduler favours. A bijection on 0 .. G-1; the
+// identity when the grid does not have that shape.
+__device__ __forceinline__ int64_t paired_segment(int64_t pos, int64_t items, int64_t hn, int64_t G) {
+  const int64_t n = items >> 3;
+  if ((items & 7) != 0 || n % (2 * hn) != 0) return pos;
+  const int64_t d = n / (2 * hn);
+  if (G % (2 * d) != 0) return pos;
+  const int64_t k = pos / (2 * d), i = pos % (2 * d);
+  return i < d ? G - 1 - d * k - i : d * k + (i - d);
+}
+
 template <int K, int VS, bool OUT_F32>
 __global__ __launch_bounds__((Split<Cfg<K, VS>>::W * kWave)) void based_chunk_readout_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float c1,
@@ -996,7 +1012,8 @@ __global__ __launch_bounds__((Split<Cfg<K, VS>>::W * kWave)) void based_chunk_re
   const int64_t item = item_of_block();
   const int64_t items = sh.B * sh.H * pl.nvs * pl.segments;
   if (item >= items) return;
-  const ItemCoords ic = decode_item(item, sh.H, pl.nvs, pl.segments);
+  ItemCoords ic = decode_item(item, sh.H, pl.nvs, pl.segments);
+  if (!pl.scanned) ic.g = paired_segment(ic.g, items, sh.H * pl.nvs, pl.segments);
   __shared__ ReadoutSmem<Cf> sm;
   const Rows rw = make_rows<K, VS>(q, k, v, sh, ic);
   const int64_t bh_v = (ic.b * sh.T * sh.H + ic.h) * sh.V + ic.vs * VS;

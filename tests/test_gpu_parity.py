@@ -64,7 +64,7 @@ def test_parity_full(B, T, H, K, V, scale, out):
     _gate(o, ref, f"B{B} T{T} H{H} K{K} V{V} scale={scale} {out}")
 
 
-@pytest.mark.parametrize("K,V", [(16, 64), (8, 128)])
+@pytest.mark.parametrize("K,V", [(16, 64), (8, 128), (16, 128)])
 @pytest.mark.parametrize("seg", [64, 128, 192, 256, 384, 100000])
 def test_parity_forced_segments(K, V, seg):
     """Every sequence split (many earlier segment sums, ragged tail, single segment) gives the answer."""
@@ -75,7 +75,7 @@ def test_parity_forced_segments(K, V, seg):
     _gate(o, ref, f"K{K} V{V} seg{seg}")
 
 
-@pytest.mark.parametrize("K,V,seg", [(16, 64, 128), (8, 128, 64)])
+@pytest.mark.parametrize("K,V,seg", [(16, 64, 128), (8, 128, 64), (16, 128, 128)])
 def test_parity_scanned_segments(K, V, seg):
     """More than 16 segments: the segment sums go through the prefix-scan kernel first."""
     from taylor_feature_map_amd import plan
@@ -86,6 +86,18 @@ def test_parity_scanned_segments(K, V, seg):
     ref = based_ref_chunked(bf16_to_f64(qb), bf16_to_f64(kb), bf16_to_f64(vb), None, 64)
     o = _run(qb, kb, vb, None, torch.bfloat16, segment_len=seg)
     _gate(o, ref, f"K{K} V{V} seg{seg} G{g}")
+
+
+@pytest.mark.parametrize("B,T,H,K,V", [(1, 1024, 4, 16, 64), (2, 1000, 4, 8, 128)])
+def test_parity_paired_segment_order(B, T, H, K, V):
+    """Grids whose read-out blocks take the segments in the paired order (segment g beside G-1-g)."""
+    from taylor_feature_map_amd import plan
+    g, _, _ = plan(B, T, H, K, V, 64)
+    assert g == 16  # B H G divisible by 8 and G by the pairing run: the reordering is active
+    qb, kb, vb = make_qkv(B, T, H, K, V, seed=11 + K)
+    ref = based_ref_direct(bf16_to_f64(qb), bf16_to_f64(kb), bf16_to_f64(vb), None)
+    o = _run(qb, kb, vb, None, torch.bfloat16, segment_len=64)
+    _gate(o, ref, f"B{B} T{T} H{H} K{K} V{V} G{g}")
 
 
 def test_deterministic_and_split_independent():
