@@ -52,10 +52,22 @@ def traffic_file(workload_name):
     return os.path.join(ROOT, "profiles", f"based_chunk_readout_traffic_{workload_name}.md")
 
 
+def kernel_code_digest(path=KERNEL_SOURCE):
+    """SHA-256 of the kernel source with comments and blank lines left out, so that the digest changes
+    when the code does and not when a comment does."""
+    import hashlib
+    import re
+    lines = []
+    for line in open(path):
+        code = re.sub(r"//.*", "", line).strip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def measured_traffic(workload_name):
     """HBM bytes per read-out launch from the committed rocprofv3 summary of this workload, or None when
-    there is none or it was taken on a different kernel source."""
-    import hashlib
+    there is none or it was taken on different kernel code."""
     path = traffic_file(workload_name)
     if not os.path.exists(path):
         return None
@@ -64,8 +76,7 @@ def measured_traffic(workload_name):
         if ":" in line and line.startswith("    "):
             key, val = line.strip().split(":", 1)
             fields[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    if fields.get("kernel_source_sha256") != sha:
+    if fields.get("kernel_code_sha256") != kernel_code_digest():
         return None
     return int(fields["traffic_bytes_per_launch"])
 

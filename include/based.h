@@ -145,11 +145,12 @@ based_status_t based_decode_step(const void* q, const void* k, const void* v,
  * ------------------------------------------------------------------------------------------------- */
 
 /* The sequence is split into `segments` pieces of `segment_len` tokens (the last may be shorter); each
- * piece of each (b, h, 64-column slice of V) is processed by one workgroup (4 wavefronts for K = 16, 2
- * for K = 8) in chunks of 64 tokens; a first kernel sums the state of every
- * piece but the last into the workspace, and the read-out of piece g starts from the sum of the sums of
- * pieces 0 .. g - 1 (with more than 16 pieces, a prefix-scan kernel forms those sums in between). Reports the plan chosen for a shape; segment_len_override > 0 forces that
- * length (rounded up to a whole number of chunks). */
+ * piece of each (b, h, group of 64 value columns, or 128 when V is a multiple of 128) is processed by one
+ * workgroup in chunks of 64 tokens (128 for 128 columns with K = 16); a first kernel sums the state of
+ * every piece but the last into the workspace, and the read-out of piece g starts from the sum of the
+ * sums of pieces 0 .. g - 1 (with more than 16 pieces, a prefix-scan kernel forms those sums in between).
+ * Reports the plan chosen for a shape; segment_len_override > 0 forces that length (rounded up to a
+ * whole number of chunks). */
 based_status_t based_forward_plan(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                   int64_t segment_len_override, int64_t* segments,
                                   int64_t* segment_len, size_t* workspace_bytes);

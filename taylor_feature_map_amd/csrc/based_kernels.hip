@@ -8,10 +8,11 @@
 // the direct polynomial (field reference_src; field perf_md describes the same split).
 //
 // Design:
-//  * Work item = (batch b, head h, 64-column slice of V, sequence segment), run by a workgroup of W
-//    wavefronts over chunks of 32 W tokens (K = 16: W = 4; K = 8: W = 2). The feature tiles of the state
-//    are split between the waves for the update; every wave reads out two 16-token query tiles of each
-//    chunk through the whole state, whose bf16 copy the waves publish to LDS after each chunk.
+//  * Work item = (batch b, head h, 64 or 128 value columns, sequence segment), run by a workgroup of W
+//    wavefronts over chunks of C tokens (see Split: K = 16 with 64 columns W = 4, C = 64; with 128
+//    columns W = 8, C = 128; K = 8: W = 2 or 4, C = 64). The feature tiles of the state are split between
+//    the waves for the update; every wave reads out its 16-token query tile(s) of each chunk through the
+//    whole state, whose bf16 copy the waves publish to LDS after each chunk.
 //  * The quadratic block is used in its symmetric form: the page allows any algebraic rearrangement that
 //    matches (field spec_md). Unordered feature pairs {a, b} are laid out on a 16-lane row as "cyclic
 //    distance" tiles: tile d holds x_n * x_{(n-d) mod 16} in lane n, so every partner is a DPP row
@@ -30,11 +31,10 @@
 //    chunk ahead into registers and staged in LDS in their natural row layout (16-byte units of V
 //    swizzled against bank conflicts); V and K with the token index along the contraction come from
 //    ds_read_b64_tr_b16 transpose reads.
-//  * Long sequences are split into segments so that all SIMDs have work: a first kernel sums
-//    phi(k)^T v per segment (every segment but the last), and the read-out of segment g starts from
-//    the sum of the sums of segments 0 .. g - 1, added in segment order at its start. With many
-//    segments a prefix-scan kernel turns the sums into those starting states first.
-//    starts each segment from its prefix state.
+//  * Long sequences are split into segments so that all SIMDs have work (two waves per SIMD): a first
+//    kernel sums phi(k)^T v per segment (every segment but the last), and the read-out of segment g
+//    starts from the sum of the sums of segments 0 .. g - 1, added in segment order at its start. With
+//    more than 16 segments a prefix-scan kernel turns the sums into those starting states first.
 //
 // MFMA lane layouts used (v_mfma_f32_16x16x32_bf16, lane l, column c = l % 16, group g = l / 16):
 //   A operand: row c, contraction slots 8g..8g+7;  B operand: column c, slots 8g..8g+7;
@@ -353,7 +353,7 @@ struct Units {
   }
 };
 
-// Buffer resource over the rows of one (b, h, value slice): base points at token 0, the range ends at
+// Buffer resource over the rows of one (b, h, value columns): base points at token 0, the range ends at
 // token T (stride_bytes per token).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t T, int64_t stride_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(T * stride_bytes),
@@ -800,7 +800,7 @@ __device__ __forceinline__ void initial_state(SA& S, const float* __restrict__ s
 
 // A state in the page's layout for one (b, h) and work item: entry (row r, item column j) of S at
 // s[r * V + j], of z at z[r]. Import when s_in is set, export (of the state after the last token) when
-// s_out is set; write_z selects the one value slice that writes z.
+// s_out is set; write_z selects the one work item of the (b, h) that writes z.
 struct StateView {
   const float* s_in;
   const float* z_in;
