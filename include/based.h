@@ -83,7 +83,9 @@ based_status_t based_forward(const void* q, const void* k, const void* v,
                              float scale, void* out, based_dtype_t out_dtype, hipStream_t stream);
 
 /* Same as based_forward, with a caller-provided device workspace of at least
- * based_forward_workspace_bytes(...) bytes (may be NULL when that is 0). No allocation is made. */
+ * based_forward_workspace_bytes(...) bytes (may be NULL when that is 0). No allocation is made and no
+ * memory is cleared with a memset: the call only launches kernels on `stream`, so it can be recorded into
+ * a HIP graph and replayed (the pointers are baked into the graph). */
 based_status_t based_forward_ws(const void* q, const void* k, const void* v,
                                 int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                 float scale, void* out, based_dtype_t out_dtype,
