@@ -55,6 +55,7 @@ def _gate(o, ref, what):
     (1, 257, 3, 8, 64, 1.0, torch.bfloat16),
     (2, 1000, 2, 16, 192, None, torch.bfloat16),
     (1, 700, 1, 8, 128, 0.35, torch.float32),
+    (1, 300, 2, 16, 512, None, torch.float32),     # widest V: four 128-column items per head
 ])
 def test_parity_full(B, T, H, K, V, scale, out):
     qb, kb, vb = make_qkv(B, T, H, K, V, seed=T + 7 * K + V)
@@ -156,6 +157,36 @@ def test_parity_benchmark_shapes_sampled(wi):
                                           bf16_to_f64(vb[b:b + 1]), w.scale, 0, h, rows))
         got.append(o[b, rows, h, :])
     _gate(np.concatenate(got), np.concatenate(want), f"{w.name} sampled rows")
+
+
+def test_parity_maximum_row_range():
+    """The largest sequence the 32-bit buffer ranges allow at H = 1, V = 64 with fp32 output:
+    T * H * V * 4 = 2^31 - 256 bytes (T = 8,388,607, a ragged last chunk), 512 segments, so the prefix
+    scan runs over 511 segment sums in many batches. Inputs: a seeded 65,536-token block repeated along
+    the sequence (the kernels do not see the repetition); outputs compared on sampled rows, each from the
+    definition over all earlier tokens."""
+    from taylor_feature_map_amd import plan
+    d = _dev()
+    B, H, K, V = 1, 1, 16, 64
+    T = (2 ** 31 - 1) // (H * V * 4)
+    g, seg_len, _ = plan(B, T, H, K, V)
+    assert g > 32 and T % 64 != 0
+    blk = 65536
+    qb, kb, vb = make_qkv(B, blk, H, K, V, seed=2024)
+    reps = -(-T // blk)
+    qb = np.tile(qb, (1, reps, 1, 1))[:, :T]
+    kb = np.tile(kb, (1, reps, 1, 1))[:, :T]
+    vb = np.tile(vb, (1, reps, 1, 1))[:, :T]
+    print(f"maximum row range: T={T} segments={g} segment_len={seg_len}", flush=True)
+    q, k, v = _to_dev(qb), _to_dev(kb), _to_dev(vb)
+    from taylor_feature_map_amd import based_forward
+    o = based_forward(q, k, v, None, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = [0, 1, 63, 64, seg_len - 1, seg_len, seg_len + 1, 3 * seg_len + 17, T // 2, T - 65, T - 64, T - 2, T - 1]
+    got = o[0, rows, 0, :].double().cpu().numpy()
+    del q, k, v, o
+    want = based_ref_direct_rows(bf16_to_f64(qb), bf16_to_f64(kb), bf16_to_f64(vb), None, 0, 0, rows)
+    _gate(got, want, f"T={T} sampled rows")
 
 
 # ------------------------------------------------------------------ argument errors through the binding
