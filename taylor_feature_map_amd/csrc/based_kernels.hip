@@ -632,30 +632,34 @@ __global__ __launch_bounds__((Split<Cfg<K, 64>>::W * kWave)) void based_segment_
 // ------------------------------------------------------------- kernel 1: prefix over segments
 
 // Used when there are too many segments for each read-out to add up its predecessors' sums: in place,
-// slot s of every (b, h, work item columns) becomes the sum of the segment sums 0..s. Slots are read in
+// slot s of every (b, h, work item columns) becomes the sum of the segment sums 0..s. One thread per four
+// consecutive state entries (a slot holds a multiple of four floats, 16-byte aligned); slots are read in
 // batches ahead of the running sum so that the loads of a batch do not wait for the stores of the previous
 // one; with up to 32 slots every load is issued before the first add.
 __global__ __launch_bounds__(256) void based_segment_scan_kernel(float* __restrict__ ws, int64_t n_bhv,
                                                                  int64_t slots, int64_t slot_floats) {
   constexpr int kBatch = 16;
+  const int64_t quads = slot_floats / 4;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= n_bhv * slot_floats) return;
-  const int64_t bhv = idx / slot_floats;
-  const int64_t e = idx - bhv * slot_floats;
+  if (idx >= n_bhv * quads) return;
+  const int64_t bhv = idx / quads;
+  const int64_t e = (idx - bhv * quads) * 4;
   float* p = ws + bhv * slots * slot_floats + e;
-  float cur[kBatch];
+  auto at = [&](int64_t s) { return reinterpret_cast<f32x4_t*>(p + s * slot_floats); };
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t cur[kBatch];
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) cur[j] = j < slots ? p[j * slot_floats] : 0.0f;
-  float run = 0.0f;
+  for (int j = 0; j < kBatch; ++j) cur[j] = j < slots ? *at(j) : zero4;
+  f32x4_t run = zero4;
   for (int64_t s0 = 0; s0 < slots; s0 += kBatch) {
-    float nxt[kBatch];
+    f32x4_t nxt[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) nxt[j] = s0 + kBatch + j < slots ? p[(s0 + kBatch + j) * slot_floats] : 0.0f;
+    for (int j = 0; j < kBatch; ++j) nxt[j] = s0 + kBatch + j < slots ? *at(s0 + kBatch + j) : zero4;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (s0 + j < slots) {
         run += cur[j];
-        p[(s0 + j) * slot_floats] = run;
+        *at(s0 + j) = run;
       }
     }
 #pragma unroll
@@ -1130,7 +1134,7 @@ hipError_t launch_segment_state(const void* k, const void* v, const Shape& sh, c
 
 hipError_t launch_segment_scan(const Shape& sh, const Plan& pl, float* ws, hipStream_t stream) {
   const int64_t n_bhv = sh.B * sh.H * pl.nvs;
-  const int64_t total = n_bhv * pl.slot_floats;
+  const int64_t total = n_bhv * (pl.slot_floats / 4);
   const int64_t blocks = (total + 255) / 256;
   hipLaunchKernelGGL(based_segment_scan_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, ws,
                      n_bhv, pl.segments - 1, pl.slot_floats);
