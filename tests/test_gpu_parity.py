@@ -101,6 +101,32 @@ def test_parity_paired_segment_order(B, T, H, K, V):
     _gate(o, ref, f"B{B} T{T} H{H} K{K} V{V} G{g}")
 
 
+def _random_cases(n=24, seed=20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        K = int(rng.choice([8, 16]))
+        V = int(rng.choice([64, 128, 192, 256]))
+        B = int(rng.integers(1, 4))
+        H = int(rng.integers(1, 6))
+        T = int(rng.integers(1, 1500))
+        seg = int(rng.choice([0, 0, 64, 128, 192, 320, 512]))
+        scale = [None, 0.3, -0.7, 0.05][int(rng.integers(0, 4))]
+        out = [torch.bfloat16, torch.float32][int(rng.integers(0, 2))]
+        cases.append((i, B, T, H, K, V, seg, scale, out))
+    return cases
+
+
+@pytest.mark.parametrize("i,B,T,H,K,V,seg,scale,out", _random_cases())
+def test_parity_random_shapes(i, B, T, H, K, V, seg, scale, out):
+    """Seeded random shapes, segment lengths, scales and output types, each compared in full with the
+    definition."""
+    qb, kb, vb = make_qkv(B, T, H, K, V, seed=500 + i)
+    ref = based_ref_direct(bf16_to_f64(qb), bf16_to_f64(kb), bf16_to_f64(vb), scale)
+    o = _run(qb, kb, vb, scale, out, segment_len=seg)
+    _gate(o, ref, f"case {i}: B{B} T{T} H{H} K{K} V{V} seg{seg} scale={scale} {out}")
+
+
 def test_deterministic_and_split_independent():
     qb, kb, vb = make_qkv(2, 3000, 4, 16, 64, seed=5)
     a = _run(qb, kb, vb, None, torch.float32)
