@@ -1,7 +1,7 @@
 """Benchmark of the causal Based forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--workload NAME|INDEX]
-                [--no-cpu-baseline] [--all] [--page-shapes]
+                [--no-cpu-baseline] [--all] [--page-shapes] [--decode B,H,K,V[;...]] [--with-state]
 
 A step is one full forward (every kernel of the path) over one batch of synthetic bf16 inputs that are
 resident in device memory before timing starts. Before the W warm-up steps, untimed steps run back to back
@@ -246,6 +246,101 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3
     return result
 
 
+def _settle(fn, settle_s):
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
+def decode_bench(B, H, K, V, steps, settle_s):
+    """The one-token recurrent step (based_decode_step) on B sequences x H heads: the state is read and
+    written once per token, so its roofline is HBM. Algorithmic bytes per step = the fp32 state and
+    normaliser read and written (8 (P V + P) per (b, h)) + q, k, v read + o written (bf16)."""
+    import torch
+
+    from taylor_feature_map_amd import _lib
+    from taylor_feature_map_amd.based import feature_dim
+    dev = torch.device("cuda:0")
+    P = feature_dim(K)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    q = torch.randn((B, H, K), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, H, K), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, H, V), generator=g, device=dev).to(torch.bfloat16)
+    S = torch.zeros((B, H, P, V), dtype=torch.float32, device=dev)
+    z = torch.zeros((B, H, P), dtype=torch.float32, device=dev)
+    o = torch.empty((B, H, V), dtype=torch.bfloat16, device=dev)
+    L = _lib.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, K, V, float("nan"), S.data_ptr(), z.data_ptr(),
+            o.data_ptr(), _lib.BASED_BF16, stream)
+
+    def step():
+        _lib.check(L.based_decode_step(*args), "based_decode_step")
+
+    _settle(step, settle_s)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = B * H * (8 * (P * V + P) + 4 * K + 2 * V + 2 * V)
+    return {"workload": f"decode_b{B}_h{H}_k{K}_v{V}", "us_per_step": us, "tokens_per_s": B / (us * 1e-6),
+            "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+def state_forward_bench(w, steps, settle_s):
+    """The forward with a state carried in and the state after the last token written out
+    (based_forward_state), against the plain forward on the same inputs."""
+    import torch
+
+    from taylor_feature_map_amd import _lib, plan
+    from taylor_feature_map_amd.based import feature_dim
+    from taylor_feature_map_amd.inputs import make_qkv_device
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv_device(w.B, w.T, w.H, w.K, w.V, w.seed, dev)
+    P = feature_dim(w.K)
+    s_in = torch.randn((w.B, w.H, P, w.V), device=dev) * 0.1
+    z_in = torch.rand((w.B, w.H, P), device=dev) + float(w.T)
+    s_out, z_out = torch.empty_like(s_in), torch.empty_like(z_in)
+    out = torch.empty((w.B, w.T, w.H, w.V), dtype=torch.bfloat16, device=dev)
+    _, _, need = plan(w.B, w.T, w.H, w.K, w.V)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    L = _lib.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    scale = float("nan") if w.scale is None else w.scale
+    base = (q.data_ptr(), k.data_ptr(), v.data_ptr(), w.B, w.T, w.H, w.K, w.V, scale, out.data_ptr(),
+            _lib.BASED_BF16)
+
+    def plain():
+        _lib.check(L.based_forward_ws(*base, ws.data_ptr(), ws.numel(), stream), "based_forward_ws")
+
+    def with_state():
+        _lib.check(L.based_forward_state(*base, s_in.data_ptr(), z_in.data_ptr(), s_out.data_ptr(),
+                                         z_out.data_ptr(), ws.data_ptr(), ws.numel(), stream),
+                   "based_forward_state")
+
+    res = {"workload": f"state_{w.name}"}
+    for name, fn in (("plain", plain), ("with_state", with_state)):
+        _settle(fn, settle_s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{name}_ms"] = e0.elapsed_time(e1) / steps
+    res["state_bytes_in_out"] = 2 * w.B * w.H * (P * w.V + P) * 4
+    return res
+
+
 def copy_probe(mib, reps):
     """A plain copy of known size: reads and writes mib MiB per launch. Profiler counters taken on it give
     the factor between counter readings and bytes moved."""
@@ -273,6 +368,10 @@ def main():
     ap.add_argument("--all", action="store_true", help="also print a line per workload to stderr")
     ap.add_argument("--page-shapes", action="store_true",
                     help="also print a line per measure and grader shape of the page to stderr")
+    ap.add_argument("--decode", default=None, metavar="B,H,K,V[;B,H,K,V...]",
+                    help="also print a line per one-token decode-step shape (stderr)")
+    ap.add_argument("--with-state", action="store_true",
+                    help="also print the forward with state in and out against the plain forward (stderr)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
     a = ap.parse_args()
@@ -307,6 +406,12 @@ def main():
                             "kernels": r["kernels"]}))
             import torch
             torch.cuda.empty_cache()
+    if a.decode:
+        for spec in a.decode.split(";"):
+            B, H, K, V = (int(x) for x in spec.split(","))
+            log(json.dumps(decode_bench(B, H, K, V, max(a.steps, 100), a.settle_ms / 1e3)))
+    if a.with_state:
+        log(json.dumps(state_forward_bench(pick_workload(a.workload), a.steps, a.settle_ms / 1e3)))
     w = pick_workload(a.workload)
     res = run_bench(w, a.steps, a.warmup, with_cpu=not a.no_cpu_baseline, settle_s=a.settle_ms / 1e3)
     print(json.dumps(res), flush=True)

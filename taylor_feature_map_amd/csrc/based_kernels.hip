@@ -1064,17 +1064,32 @@ __device__ __forceinline__ float phi_row(const float* x, int r) {
   return x[i / K] * x[i % K] * kRSqrt2;
 }
 
-// One workgroup per (b, h): S += phi(k) v^T and z += phi(k) in place (the page's layout, fp32), then
-// o = phi(scale q) S / (phi(scale q) z + 1e-6). Memory-bound: every state entry is read and written once.
-template <int K>
-__global__ __launch_bounds__(256) void based_decode_step_kernel(const u16* __restrict__ q, const u16* __restrict__ k,
-                                                                const u16* __restrict__ v, int64_t V, float sigma,
-                                                                float* __restrict__ S, float* __restrict__ z,
-                                                                void* __restrict__ out, bool out_f32) {
+// Sum of a float over the 64 lanes of a wave (every lane gets the total).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+
+// One workgroup of NT threads per (b, h): S += phi(k) v^T and z += phi(k) in place (the page's layout,
+// fp32), then o = phi(scale q) S / (phi(scale q) z + 1e-6). Memory-bound: every state entry is read and
+// written once. A block of 64 value columns is 16 lanes of 16-byte accesses per state row; the NT / 16
+// row groups take every (NT / 16)-th row, and all of a thread's rows are loaded before any is stored so
+// that the loads are in flight together. Partial numerators meet in LDS (two buffers, one barrier per
+// column block).
+template <int K, int NT>
+__global__ __launch_bounds__(NT) void based_decode_step_kernel(const u16* __restrict__ q, const u16* __restrict__ k,
+                                                               const u16* __restrict__ v, int64_t V, float sigma,
+                                                               float* __restrict__ S, float* __restrict__ z,
+                                                               void* __restrict__ out, bool out_f32) {
   constexpr int P = 1 + K + K * K;
+  constexpr int RG = NT / 16;             // row groups
+  constexpr int NR = (P + RG - 1) / RG;   // rows per thread
+  constexpr int NW = NT / kWave;
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
-  __shared__ float sq[K], sk[K], part_num[4][64], part_den[256], den_total;
+  __shared__ float sq[K], sk[K], part_den[NW];
+  __shared__ f32x4_t part[2][RG][16];
   if (tid < K) {
     sq[tid] = sigma * lo_f(q[bh * K + tid]);
     sk[tid] = lo_f(k[bh * K + tid]);
@@ -1083,39 +1098,62 @@ __global__ __launch_bounds__(256) void based_decode_step_kernel(const u16* __res
   float* Sb = S + bh * P * V;
   float* zb = z + bh * P;
   float dp = 0.0f;
-  for (int r = tid; r < P; r += 256) {
+  for (int r = tid; r < P; r += NT) {
     const float nz = zb[r] + phi_row<K>(sk, r);
     zb[r] = nz;
     dp += phi_row<K>(sq, r) * nz;
   }
-  part_den[tid] = dp;
-  __syncthreads();
-  if (tid == 0) {
-    float d = 0.0f;
-    for (int i = 0; i < 256; ++i) d += part_den[i];
-    den_total = d;
+  dp = wave_sum(dp);
+  if ((tid & (kWave - 1)) == 0) part_den[tid / kWave] = dp;
+  const int cq = tid & 15, rg = tid >> 4;
+  float pk[NR], pq[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int r = rg + RG * i;
+    pk[i] = r < P ? phi_row<K>(sk, r) : 0.0f;
+    pq[i] = r < P ? phi_row<K>(sq, r) : 0.0f;
   }
-  const int cl = tid & 63, part = tid >> 6;
-  for (int64_t c0 = 0; c0 < V; c0 += 64) {
-    const int64_t col = c0 + cl;
-    const float vv = lo_f(v[bh * V + col]);
-    float num = 0.0f;
-    for (int r = part; r < P; r += 4) {
-      const float sn = Sb[r * V + col] + phi_row<K>(sk, r) * vv;
-      Sb[r * V + col] = sn;
-      num += phi_row<K>(sq, r) * sn;
+  for (int64_t c0 = 0, blk = 0; c0 < V; c0 += 64, ++blk) {
+    const int64_t col = c0 + 4 * cq;
+    const uint2 vr = *reinterpret_cast<const uint2*>(v + bh * V + col);
+    const float v0 = lo_f(vr.x), v1 = hi_f(vr.x), v2 = lo_f(vr.y), v3 = hi_f(vr.y);
+    f32x4_t s[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = rg + RG * i;
+      if (r < P) s[i] = *reinterpret_cast<const f32x4_t*>(Sb + r * V + col);
     }
-    part_num[part][cl] = num;
-    __syncthreads();  // also publishes den_total on the first pass
-    if (part == 0) {
-      const float o = (((part_num[0][cl] + part_num[1][cl]) + part_num[2][cl]) + part_num[3][cl]) / (den_total + 1e-6f);
-      if (out_f32) {
-        static_cast<float*>(out)[bh * V + col] = o;
-      } else {
-        static_cast<u16*>(out)[bh * V + col] = static_cast<u16>(pack2(o, 0.0f) & 0xffffu);
+    f32x4_t num = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = rg + RG * i;
+      if (r < P) {
+        s[i][0] += pk[i] * v0;
+        s[i][1] += pk[i] * v1;
+        s[i][2] += pk[i] * v2;
+        s[i][3] += pk[i] * v3;
+        *reinterpret_cast<f32x4_t*>(Sb + r * V + col) = s[i];
+        num[0] += pq[i] * s[i][0];
+        num[1] += pq[i] * s[i][1];
+        num[2] += pq[i] * s[i][2];
+        num[3] += pq[i] * s[i][3];
       }
     }
-    __syncthreads();
+    part[blk & 1][rg][cq] = num;
+    __syncthreads();  // also publishes part_den on the first block
+    if (tid < 64) {
+      float n = 0.0f;
+      for (int g = 0; g < RG; ++g) n += part[blk & 1][g][tid >> 2][tid & 3];
+      float den = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) den += part_den[w];
+      const float o = n / (den + 1e-6f);
+      if (out_f32) {
+        static_cast<float*>(out)[bh * V + c0 + tid] = o;
+      } else {
+        static_cast<u16*>(out)[bh * V + c0 + tid] = static_cast<u16>(pack2(o, 0.0f) & 0xffffu);
+      }
+    }
   }
 }
 
@@ -1160,14 +1198,17 @@ hipError_t launch_chunk_readout(const void* q, const void* k, const void* v, con
   return hipGetLastError();
 }
 
+// Eight waves per (b, h): measured against four and sixteen over B x H from 64 to 8192 pairs, it is the
+// fastest or within 6% of it everywhere.
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t K,
                               int64_t V, float sigma, float* S, float* z, void* out, bool out_f32, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(B * H)), block(256);
+  constexpr int NT = 512;
+  const dim3 grid(static_cast<unsigned>(B * H)), block(NT);
   if (K == 16) {
-    hipLaunchKernelGGL(based_decode_step_kernel<16>, grid, block, 0, stream, static_cast<const u16*>(q),
+    hipLaunchKernelGGL((based_decode_step_kernel<16, NT>), grid, block, 0, stream, static_cast<const u16*>(q),
                        static_cast<const u16*>(k), static_cast<const u16*>(v), V, sigma, S, z, out, out_f32);
   } else {
-    hipLaunchKernelGGL(based_decode_step_kernel<8>, grid, block, 0, stream, static_cast<const u16*>(q),
+    hipLaunchKernelGGL((based_decode_step_kernel<8, NT>), grid, block, 0, stream, static_cast<const u16*>(q),
                        static_cast<const u16*>(k), static_cast<const u16*>(v), V, sigma, S, z, out, out_f32);
   }
   return hipGetLastError();

@@ -140,3 +140,24 @@ def test_decode_from_empty_state_matches_oracle_step():
         torch.cuda.synchronize()
         _gate(_np(o), o_ref, f"decode step {t}")
     _state_gate((_np(state[0]), _np(state[1])), st, "decode state")
+
+
+@pytest.mark.parametrize("K,V", [(16, 512), (8, 320)])
+def test_decode_steps_many_value_blocks(K, V):
+    """Decode steps with many 64-column blocks per (b, h) (the kernel's partial numerators alternate between
+    two LDS buffers, so eight and five blocks reuse each several times), from a state carried in from a
+    prefix, against the oracle's steps."""
+    from taylor_feature_map_amd import based_decode_step
+    B, H, T0, steps = 2, 3, 40, 3
+    qb, kb, vb = make_qkv(B, T0 + steps, H, K, V, seed=K * V)
+    q, k, v = bf16_to_f64(qb), bf16_to_f64(kb), bf16_to_f64(vb)
+    _, st = based_ref_chunked_state(q[:, :T0], k[:, :T0], v[:, :T0], None, None)
+    state = (_f32(st[0]), _f32(st[1]))
+    for t in range(T0, T0 + steps):
+        o_ref, st = based_ref_decode_step(q[:, t], k[:, t], v[:, t], st, None)
+        o = based_decode_step(_to_dev(qb[:, t]), _to_dev(kb[:, t]), _to_dev(vb[:, t]), state,
+                              out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        print(f"decode K{K} V{V} step {t}", flush=True)
+        _gate(_np(o), o_ref, f"decode K{K} V{V} step {t}")
+    _state_gate((_np(state[0]), _np(state[1])), st, f"decode state K{K} V{V}")
