@@ -125,7 +125,28 @@ def cpu_baseline(w, qb, kb, vb, budget_s=10.0):
                   f"{t_total:.2f} s; tokens/s scaled to the whole B*T workload",
         "seconds": round(t_total, 3),
         "canonical_gflops": canonical_flops(1, w.T, done, w.K, w.V) / t_total / 1e9,
+        "cpu_model": _cpu_model(),
+        "blas": _blas_name(),
     }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _blas_name():
+    try:
+        deps = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{deps.get('name')} {deps.get('version')}"
+    except Exception:
+        return None
 
 
 def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3):
@@ -192,6 +213,17 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3
     n_dom, ms_dom = timer.read(Timer.READOUT)
     dom_us = ms_dom * 1e3 / n_dom
 
+    # Single steps, each bracketed by HIP events on the launch stream: median and minimum.
+    single = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        single.append(e0.elapsed_time(e1))
+
     # Cold-cache steps: a 512 MiB write between steps evicts L2 and the Infinity Cache.
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     cold = []
@@ -236,14 +268,28 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3
         "path_hbm_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "ms_per_step_with_kernel_events": ms_instrumented,
+        "ms_per_step_single_median": float(np.median(single)),
+        "ms_per_step_single_min": float(np.min(single)),
         "ms_per_step_cold_median": float(np.median(cold)) if cold else None,
+        "ms_per_step_cold_min": float(np.min(cold)) if cold else None,
         "kernels": per_kernel,
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+        "device": device_info(props),
     }
     if with_cpu:
         result["cpu_baseline"] = cpu_baseline(w, qb, kb, vb)
     return result
+
+
+def device_info(props):
+    """Name, compute units, peak shader clock and L2 size of cuda:0 as HIP reports them."""
+    import ctypes
+
+    from taylor_feature_map_amd import _lib
+    cus, khz, l2 = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _lib.check(_lib.lib().based_device_info(0, ctypes.byref(cus), ctypes.byref(khz), ctypes.byref(l2)),
+               "based_device_info")
+    return {"name": props.name, "cus": cus.value, "peak_clock_mhz": khz.value / 1e3, "l2_bytes": l2.value,
+            "arch": getattr(props, "gcnArchName", "")}
 
 
 def _settle(fn, settle_s):

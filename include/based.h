@@ -172,6 +172,10 @@ void based_timer_set_kernel_mask(based_timer* timer, unsigned mask);
  * 1 = segment prefix scan, 2 = chunked read-out), the number of recorded launches and their summed
  * duration in milliseconds. */
 based_status_t based_timer_read(based_timer* timer, int kernel_id, int* launches, double* total_ms);
+/* Properties of HIP device `device` that measurements are reported with: compute units, peak shader
+ * clock in kHz, L2 cache bytes (per device as HIP reports it). Any output pointer may be NULL.
+ * Errors: BASED_ERR_HIP when the device cannot be queried. */
+based_status_t based_device_info(int device, int* compute_units, int* peak_clock_khz, int* l2_bytes);
 /* Static name of kernel `kernel_id` as it appears in profiler traces, or NULL. */
 const char* based_kernel_name(int kernel_id);
 

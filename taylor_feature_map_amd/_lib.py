@@ -37,6 +37,8 @@ SIGNATURES = {
     "based_timer_read": (ctypes.c_int, [_vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_double)]),
     "based_kernel_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "based_device_info": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                         ctypes.POINTER(ctypes.c_int)]),
     "based_forward_ex": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp,
                                         ctypes.c_int, _vp, ctypes.c_size_t, _i64, _vp, _vp]),
     "based_feature_dim": (_i64, [_i64]),

@@ -348,6 +348,21 @@ based_status_t based_timer_read(based_timer* timer, int kernel_id, int* launches
   return ok();
 }
 
+based_status_t based_device_info(int device, int* compute_units, int* peak_clock_khz, int* l2_bytes) {
+  const struct {
+    hipDeviceAttribute_t attr;
+    int* dst;
+  } q[3] = {{hipDeviceAttributeMultiprocessorCount, compute_units},
+            {hipDeviceAttributeClockRate, peak_clock_khz},
+            {hipDeviceAttributeL2CacheSize, l2_bytes}};
+  for (const auto& e : q) {
+    if (!e.dst) continue;
+    const hipError_t err = hipDeviceGetAttribute(e.dst, e.attr, device);
+    if (err != hipSuccess) return fail(BASED_ERR_HIP, std::string("device info: ") + hipGetErrorString(err));
+  }
+  return ok();
+}
+
 const char* based_kernel_name(int kernel_id) {
   switch (kernel_id) {
     case 0: return "based_segment_state_kernel";
