@@ -49,7 +49,8 @@ extern "C" {
 typedef enum {
     BASED_OK = 0,
     BASED_ERR_INVALID_ARGUMENT = 1,   /* null pointer, non-positive size, misalignment, overlap, inf scale */
-    BASED_ERR_UNSUPPORTED = 2,        /* K or V outside the supported set, or T * H * V too large */
+    BASED_ERR_UNSUPPORTED = 2,        /* K or V outside the supported set, T * H * V too large, or 2^30 or more
+                                         work items (B * H * column groups * segments) */
     BASED_ERR_HIP = 3,                /* a HIP runtime call or kernel launch failed */
     BASED_ERR_OUT_OF_MEMORY = 4,      /* the workspace could not be allocated */
     BASED_ERR_WORKSPACE_TOO_SMALL = 5 /* the caller's workspace is smaller than required */

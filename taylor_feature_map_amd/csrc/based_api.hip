@@ -32,7 +32,10 @@ based_status_t ok() {
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;  // keeps every byte offset far from int64 overflow
 constexpr int64_t kTargetWaves = 2048;           // 256 CUs x 4 SIMDs x 2 resident waves
-constexpr int64_t kMinSegment = 256;             // shorter segments cost more in state traffic than they gain
+// Segments shorter than this are used only up to kMaxShortSegments of them: with more, the start-up reads
+// of the earlier segments' sums (or a scan kernel) cost more than the shorter chains gain.
+constexpr int64_t kShortSegment = 256;
+constexpr int64_t kMaxShortSegments = 8;
 constexpr int64_t kMaxRowRange = 0x7fffffff;     // bytes addressable through one 32-bit buffer range
 
 based_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
@@ -62,14 +65,31 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
     const int64_t g_target = (kTargetWaves + waves - 1) / waves;
     L = (sh.T + g_target - 1) / g_target;
     L = (L + ck - 1) / ck * ck;
-    if (L < kMinSegment) L = kMinSegment;
+    // At least one chunk per segment for K = 8 and two for K = 16, whose segment sums are 3.3 times
+    // larger, so that each further segment costs more start-up reads (measured on short sequences).
+    const int64_t l_min = (sh.K == 16 ? 2 : 1) * ck;
+    if (L < l_min) L = l_min;
+    if (L < kShortSegment && (sh.T + L - 1) / L > kMaxShortSegments) L = (kShortSegment + ck - 1) / ck * ck;
   }
   if (L > t_round) L = t_round;
   pl.seg_len = L;
   pl.segments = (sh.T + L - 1) / L;
   pl.slot_floats = based::state_slot_floats(sh.K, pl.item_cols);
   pl.scanned = pl.segments > based::kMaxSummedSegments;
+  // XCD-affine items when the (b, columns, h) pairs split evenly over the 8 XCDs and each XCD's run of
+  // heads covers whole 128-byte lines of the q and k rows (64 / K heads per line).
+  const int64_t pairs = sh.B * sh.H * pl.nvs, ppx = pairs / 8, line_heads = 64 / sh.K;
+  pl.affine = pairs % 8 == 0 && (ppx % sh.H == 0 || (sh.H % line_heads == 0 && ppx % line_heads == 0));
   return pl;
+}
+
+// The kernels number their work items in 32 bits: (b, h, columns, segment) for the read-out, twice as many
+// 64-column halves per segment (but one segment fewer) for the state sums.
+based_status_t check_items(const Shape& sh, const Plan& pl) {
+  const int64_t pairs = sh.B * sh.H * pl.nvs;
+  if (pairs > based::kMaxItems / pl.segments / 2)
+    return fail(BASED_ERR_UNSUPPORTED, "too many work items: B * H * (V / columns) * segments must stay below 2^30");
+  return BASED_OK;
 }
 
 size_t workspace_bytes(const Shape& sh, const Plan& pl) {
@@ -142,6 +162,7 @@ based_status_t run(const void* q, const void* k, const void* v, const Shape& sh,
     return fail(BASED_ERR_INVALID_ARGUMENT, "out overlaps the state input");
 
   const Plan pl = make_plan(sh, seg_override);
+  if (based_status_t s = check_items(sh, pl)) return s;
   const size_t need = workspace_bytes(sh, pl);
   if (!allocate) {
     if (need > 0 && !ws) return fail(BASED_ERR_WORKSPACE_TOO_SMALL, "workspace required but NULL");
@@ -229,6 +250,7 @@ based_status_t based_forward_plan(int64_t B, int64_t T, int64_t H, int64_t K, in
   if (segment_len_override < 0) return fail(BASED_ERR_INVALID_ARGUMENT, "segment length override must be >= 0");
   const Shape sh{B, T, H, K, V};
   const Plan pl = make_plan(sh, segment_len_override);
+  if (based_status_t s = check_items(sh, pl)) return s;
   if (segments) *segments = pl.segments;
   if (segment_len) *segment_len = pl.seg_len;
   if (ws_bytes) *ws_bytes = workspace_bytes(sh, pl);
@@ -271,6 +293,7 @@ based_status_t based_decode_step(const void* q, const void* k, const void* v, in
                                  int64_t V, float scale, float* state, float* norm, void* out,
                                  based_dtype_t out_dtype, hipStream_t stream) {
   if (based_status_t s = check_shape(B, 1, H, K, V)) return s;
+  if (B * H > based::kMaxItems) return fail(BASED_ERR_UNSUPPORTED, "B * H must stay below 2^31 for the decode step");
   if (!q || !k || !v || !out || !state || !norm) return fail(BASED_ERR_INVALID_ARGUMENT, "null pointer");
   if (out_dtype != BASED_BF16 && out_dtype != BASED_F32)
     return fail(BASED_ERR_INVALID_ARGUMENT, "out_dtype must be BASED_BF16 or BASED_F32");

@@ -22,7 +22,11 @@ struct Shape {
 struct Plan {
   int64_t segments, seg_len, nvs, item_cols, slot_floats;
   bool scanned;
+  bool affine;  // XCD-affine work items (every segment of a (b, h, columns) pair on one XCD)
 };
+
+// Upper bound on the work items (blocks) of one launch; below it all item index arithmetic fits in 32 bits.
+constexpr int64_t kMaxItems = (int64_t(1) << 31) - 8;
 
 // Most segments for which each read-out adds up its predecessors' sums itself (beyond this, the
 // quadratic number of slot reads costs more than a scan kernel).

@@ -103,12 +103,6 @@ __device__ __forceinline__ u32x2_t lds_tr16(const u16* p) {
 // Work item of a block: blocks are dealt to the 8 XCDs round robin, so block x runs on XCD x % 8.
 // Consecutive items (neighbouring heads of one batch and segment, which share cache lines of q and k)
 // are given to one XCD so that they meet in its L2.
-__device__ __forceinline__ int64_t item_of_block() {
-  const int64_t per = gridDim.x >> 3;
-  const int64_t x = blockIdx.x;
-  return (x & 7) * per + (x >> 3);
-}
-
 // ------------------------------------------------------------------------- feature tiles (phi)
 
 template <int K>
@@ -485,15 +479,88 @@ struct ItemCoords {
   int64_t b, h, vs, g;
 };
 
-__device__ __forceinline__ ItemCoords decode_item(int64_t item, int64_t H, int64_t NVS, int64_t G) {
+// Work items of a launch. Block x runs on XCD x % 8. The grid holds the items rounded up to a multiple of 8
+// (fewer than 2^31, so the index arithmetic is 32-bit). By default XCD x takes the x-th eighth of the
+// items, numbered (b, segment, columns, h) with h fastest, so neighbouring heads of one (b, segment), whose
+// q and k rows share cache lines, meet in one L2. With pl.affine (the host sets it when the
+// (b, columns, h) pairs divide evenly over the XCDs in runs of whole 128-byte q/k lines) XCD x takes a
+// contiguous run of pairs with all of their segments, in the state kernel and the read-out alike, so a
+// segment sum is read by the XCD that wrote it.
+__device__ __forceinline__ ItemCoords decode_item(uint32_t item, uint32_t H, uint32_t NVS, uint32_t G) {
   ItemCoords ic;
   ic.h = item % H;
-  int64_t r = item / H;
+  uint32_t r = item / H;
   ic.vs = r % NVS;
   r /= NVS;
   ic.g = r % G;
   ic.b = r / G;
   return ic;
+}
+
+__device__ __forceinline__ uint32_t default_item() {
+  const uint32_t x = blockIdx.x;
+  return (x & 7) * (gridDim.x >> 3) + (x >> 3);
+}
+
+// Segment order of the read-out blocks when each work item adds up its predecessors' sums (the start-up
+// of segment g reads g sums). Blocks are dealt to the CUs of an XCD in order, one per CU first, so the two
+// workgroups sharing a CU are the j-th and (j + n/2)-th of the XCD's n blocks: d = n / (2 H NVS) segment
+// positions apart. Positions are taken in runs of 2d as [G-1-dk .. G-d-dk, dk .. dk+d-1], which puts
+// segment g next to segment G-1-g: one of the two starts computing at once while the other reads, and the
+// long start-up goes to the older workgroup, which the scheduler favours. A bijection on 0 .. G-1; the
+// identity when the grid does not have that shape.
+__device__ __forceinline__ uint32_t paired_segment(uint32_t pos, uint32_t items, uint32_t hn, uint32_t G) {
+  const uint32_t n = items >> 3;
+  if ((items & 7) != 0 || n % (2 * hn) != 0) return pos;
+  const uint32_t d = n / (2 * hn);
+  if (G % (2 * d) != 0) return pos;
+  const uint32_t k = pos / (2 * d), i = pos % (2 * d);
+  return i < d ? G - 1 - d * k - i : d * k + (i - d);
+}
+
+// Read-out item of this block; false for the padding blocks past the last item.
+__device__ __forceinline__ bool readout_item(const Shape& sh, const Plan& pl, ItemCoords& ic) {
+  const uint32_t H = static_cast<uint32_t>(sh.H), NVS = static_cast<uint32_t>(pl.nvs);
+  const uint32_t G = static_cast<uint32_t>(pl.segments);
+  const uint32_t pairs = static_cast<uint32_t>(sh.B) * H * NVS;
+  if (pl.affine) {  // the grid is exactly pairs * G blocks
+    const uint32_t x = blockIdx.x, ppx = pairs >> 3, j = x >> 3;
+    const uint32_t pair = (x & 7) * ppx + j % ppx, s = j / ppx;
+    ic.h = pair % H;
+    ic.vs = (pair / H) % NVS;
+    ic.b = pair / (H * NVS);
+    // the CU pairing of segments as in paired_segment, with runs of one
+    ic.g = (!pl.scanned && (G & 1) == 0) ? (s < G / 2 ? G - 1 - s : s - G / 2) : s;
+    return true;
+  }
+  const uint32_t item = default_item();
+  if (item >= pairs * G) return false;
+  ic = decode_item(item, H, NVS, G);
+  if (!pl.scanned) ic.g = paired_segment(static_cast<uint32_t>(ic.g), pairs * G, H * NVS, G);
+  return true;
+}
+
+// State item of this block (64-column halves: pair p of the read-out is halves p * HALVES ..); false for
+// padding blocks.
+template <int HALVES>
+__device__ __forceinline__ bool state_item(const Shape& sh, const Plan& pl, ItemCoords& ic) {
+  const uint32_t H = static_cast<uint32_t>(sh.H), NVS = static_cast<uint32_t>(pl.nvs);
+  const uint32_t G1 = static_cast<uint32_t>(pl.segments - 1);
+  const uint32_t pairs = static_cast<uint32_t>(sh.B) * H * NVS;
+  if (pl.affine) {  // the grid is exactly pairs * HALVES * G1 blocks
+    const uint32_t x = blockIdx.x, ppx = (pairs >> 3) * HALVES, j = x >> 3;
+    const uint32_t p = (x & 7) * ppx + j % ppx;
+    const uint32_t pr = p / HALVES;
+    ic.h = pr % H;
+    ic.vs = (pr / H) % NVS * HALVES + p % HALVES;
+    ic.b = pr / (H * NVS);
+    ic.g = j / ppx;
+    return true;
+  }
+  const uint32_t item = default_item();
+  if (item >= pairs * HALVES * G1) return false;
+  ic = decode_item(item, H, NVS * HALVES, G1);
+  return true;
 }
 
 // ic.vs counts work items of VS columns.
@@ -603,18 +670,15 @@ __device__ __forceinline__ void segment_state_body(StateSmem<SC>& sm, const Rows
   }
 }
 
-// Work items of 64 columns (pl.nvs64 per (b, h)); the slot belongs to the read-out item of IVS columns that
+// Work items of 64 columns (pl.nvs * IVS / 64 per (b, h)); the slot belongs to the read-out item of IVS columns that
 // contains them.
 template <int K, int IVS>
 __global__ __launch_bounds__((Split<Cfg<K, 64>>::W * kWave)) void based_segment_state_kernel(
     const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float* __restrict__ ws) {
   using SC = Cfg<K, 64>;
   constexpr int HALVES = IVS / 64;
-  const int64_t item = item_of_block();
-  const int64_t nvs64 = pl.nvs * HALVES;
-  const int64_t items = sh.B * sh.H * nvs64 * (pl.segments - 1);
-  if (item >= items) return;
-  const ItemCoords ic = decode_item(item, sh.H, nvs64, pl.segments - 1);
+  ItemCoords ic;
+  if (!state_item<HALVES>(sh, pl, ic)) return;
   __shared__ StateSmem<SC> sm;
   const Rows rw = make_rows<K, 64>(k, k, v, sh, ic);
   const int64_t t_begin = ic.g * pl.seg_len;
@@ -992,32 +1056,14 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw
   }
 }
 
-// Segment order of the read-out blocks when each work item adds up its predecessors' sums (the start-up
-// of segment g reads g sums). Blocks are dealt to the CUs of an XCD in order, one per CU first, so the two
-// workgroups sharing a CU are the j-th and (j + n/2)-th of the XCD's n blocks: d = n / (2 H NVS) segment
-// positions apart. Positions are taken in runs of 2d as [G-1-dk .. G-d-dk, dk .. dk+d-1], which puts
-// segment g next to segment G-1-g: one of the two starts computing at once while the other reads, and the
-// long start-up goes to the older workgroup, which the scheduler favours. A bijection on 0 .. G-1; the
-// identity when the grid does not have that shape.
-__device__ __forceinline__ int64_t paired_segment(int64_t pos, int64_t items, int64_t hn, int64_t G) {
-  const int64_t n = items >> 3;
-  if ((items & 7) != 0 || n % (2 * hn) != 0) return pos;
-  const int64_t d = n / (2 * hn);
-  if (G % (2 * d) != 0) return pos;
-  const int64_t k = pos / (2 * d), i = pos % (2 * d);
-  return i < d ? G - 1 - d * k - i : d * k + (i - d);
-}
 
 template <int K, int VS, bool OUT_F32>
 __global__ __launch_bounds__((Split<Cfg<K, VS>>::W * kWave)) void based_chunk_readout_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float c1,
     float c2, float sigma, const float* __restrict__ ws, void* __restrict__ out, StateIO io) {
   using Cf = Cfg<K, VS>;
-  const int64_t item = item_of_block();
-  const int64_t items = sh.B * sh.H * pl.nvs * pl.segments;
-  if (item >= items) return;
-  ItemCoords ic = decode_item(item, sh.H, pl.nvs, pl.segments);
-  if (!pl.scanned) ic.g = paired_segment(ic.g, items, sh.H * pl.nvs, pl.segments);
+  ItemCoords ic;
+  if (!readout_item(sh, pl, ic)) return;
   __shared__ ReadoutSmem<Cf> sm;
   const Rows rw = make_rows<K, VS>(q, k, v, sh, ic);
   const int64_t bh_v = (ic.b * sh.T * sh.H + ic.h) * sh.V + ic.vs * VS;

@@ -1,0 +1,47 @@
+"""CPU checks of the work plan (`based_forward_plan`, host code, no GPU): for any shape the segments are
+whole chunks that cover the sequence exactly, segments shorter than 256 tokens come at most eight at a time,
+and the shapes whose plans were chosen by measurement keep them."""
+import pytest
+
+hypothesis = pytest.importorskip("hypothesis")
+from hypothesis import assume, given, settings, strategies as st  # noqa: E402
+
+from taylor_feature_map_amd import plan  # noqa: E402
+
+
+def chunk(K, V):
+    return 128 if (K == 16 and V % 128 == 0) else 64
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.integers(1, 16), st.integers(1, 200000), st.integers(1, 64), st.sampled_from([8, 16]),
+       st.sampled_from([64, 128, 192, 256, 512]))
+def test_plan_invariants(B, T, H, K, V):
+    assume(T * H * V * 4 <= 2 ** 31 - 1)  # the library's 32-bit row ranges
+    G, L, ws = plan(B, T, H, K, V)
+    C = chunk(K, V)
+    assert L % C == 0 and L >= C
+    assert G == -(-T // L) and (G - 1) * L < T <= G * L
+    assert G <= 8 or L >= 256, "more than eight segments shorter than 256 tokens"
+    if G > 1:
+        assert L >= (2 if K == 16 else 1) * C
+    assert (ws == 0) == (G == 1)
+
+
+@pytest.mark.parametrize("shape,G,L", [
+    ((1, 512, 2, 8, 64), 8, 64),          # short K = 8 sequence: one chunk per segment
+    ((2, 512, 8, 16, 64), 4, 128),        # short K = 16 sequence: two chunks per segment
+    ((1, 256, 4, 16, 128), 1, 256),       # two 128-token chunks: one kernel
+    ((1, 4096, 16, 8, 128), 16, 256),     # at most eight segments shorter than 256 tokens
+    ((2, 2048, 8, 16, 64), 8, 256),
+    ((4, 8192, 16, 16, 64), 8, 1024),     # two waves per SIMD
+    ((1, 65000, 16, 16, 64), 32, 2048),   # long sequence: scanned segment sums
+])
+def test_measured_plans(shape, G, L):
+    assert plan(*shape)[:2] == (G, L)
+
+
+def test_forced_segment_length_rounds_to_chunks():
+    assert plan(1, 1000, 2, 16, 64, 100)[:2] == (8, 128)
+    assert plan(1, 1000, 2, 16, 128, 100)[:2] == (8, 128)
+    assert plan(1, 1000, 2, 16, 64, 5000)[:2] == (1, 1024)
