@@ -432,8 +432,13 @@ def main():
     if a.steps < 1 or a.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
     if a.all:
+        import dataclasses
+
         from taylor_feature_map_amd.inputs import WORKLOADS
-        for w in WORKLOADS:
+        head = pick_workload(None)
+        # every workload, then the headline shape again with fp32 output as a secondary row
+        extra = dataclasses.replace(head, name=head.name + "_f32out", out_dtype="f32")
+        for w in list(WORKLOADS) + [extra]:
             r = run_bench(w, a.steps, a.warmup, with_cpu=False, settle_s=a.settle_ms / 1e3)
             log(json.dumps({"workload": w.name, "ms_per_step": r["ms_per_step"],
                             "cold_ms": r["ms_per_step_cold_median"], "tokens_per_s": r["value"],
