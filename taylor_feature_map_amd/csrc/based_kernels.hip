@@ -35,6 +35,10 @@
 //    kernel sums phi(k)^T v per segment (every segment but the last), and the read-out of segment g
 //    starts from the sum of the sums of segments 0 .. g - 1, added in segment order at its start. With
 //    more than 16 segments a prefix-scan kernel turns the sums into those starting states first.
+//  * Work items are placed on the 8 XCDs so that shared q/k cache lines, and where the heads allow it all
+//    segments of a (b, h) and hence the segment sums, stay in one XCD's L2 (readout_item, state_item).
+//  * The one-token decode step is a separate, purely memory-bound kernel over the state in the page's
+//    layout (based_decode_step_kernel).
 //
 // MFMA lane layouts used (v_mfma_f32_16x16x32_bf16, lane l, column c = l % 16, group g = l / 16):
 //   A operand: row c, contraction slots 8g..8g+7;  B operand: column c, slots 8g..8g+7;
