@@ -31,6 +31,7 @@ based_status_t ok() {
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;  // keeps every byte offset far from int64 overflow
+constexpr int64_t kCUs = 256;                    // MI355X compute units
 constexpr int64_t kTargetWaves = 2048;           // 256 CUs x 4 SIMDs x 2 resident waves
 // Segments shorter than this are used only up to kMaxShortSegments of them: with more, the start-up reads
 // of the earlier segments' sums (or a scan kernel) cost more than the shorter chains gain.
@@ -61,10 +62,19 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
   if (seg_override > 0) {
     L = (seg_override + ck - 1) / ck * ck;
   } else {
-    const int64_t waves = sh.B * sh.H * pl.nvs * based::waves_per_item(sh.K, pl.item_cols);
-    const int64_t g_target = (kTargetWaves + waves - 1) / waves;
-    L = (sh.T + g_target - 1) / g_target;
-    L = (L + ck - 1) / ck * ck;
+    const int64_t pairs = sh.B * sh.H * pl.nvs;
+    const int64_t waves = pairs * based::waves_per_item(sh.K, pl.item_cols);
+    if (pairs >= kCUs && waves >= kTargetWaves / 2) {
+      // The (b, h, columns) items alone give every CU a workgroup and every SIMD a wave: one segment, no
+      // state pass (a second wave per SIMD gains less than the state pass over half the keys costs).
+      L = t_round;
+    } else {
+      // Two waves per SIMD, except K = 8 with 128 columns, whose read-out is closest to memory-bound: one.
+      const int64_t target = (sh.K == 8 && pl.item_cols == 128) ? kTargetWaves / 2 : kTargetWaves;
+      const int64_t g_target = (target + waves - 1) / waves;
+      L = (sh.T + g_target - 1) / g_target;
+      L = (L + ck - 1) / ck * ck;
+    }
     // At least one chunk per segment for K = 8 and two for K = 16, whose segment sums are 3.3 times
     // larger, so that each further segment costs more start-up reads (measured on short sequences).
     const int64_t l_min = (sh.K == 16 ? 2 : 1) * ck;

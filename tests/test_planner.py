@@ -35,6 +35,12 @@ def test_plan_invariants(B, T, H, K, V):
     ((1, 4096, 16, 8, 128), 16, 256),     # at most eight segments shorter than 256 tokens
     ((2, 2048, 8, 16, 64), 8, 256),
     ((4, 8192, 16, 16, 64), 8, 1024),     # two waves per SIMD
+    ((4, 8192, 16, 8, 64), 16, 512),      # K = 8 with 64 columns: two waves per SIMD as well
+    ((4, 16384, 32, 8, 128), 2, 8192),    # K = 8 with 128 columns: one wave per SIMD
+    ((1, 32768, 32, 8, 128), 8, 4096),
+    ((8, 16384, 32, 16, 64), 1, 16384),   # the items alone fill every CU: no state pass
+    ((8, 16384, 32, 8, 128), 1, 16384),
+    ((16, 2048, 16, 16, 64), 1, 2048),
     ((1, 65000, 16, 16, 64), 32, 2048),   # long sequence: scanned segment sums
 ])
 def test_measured_plans(shape, G, L):
