@@ -44,7 +44,8 @@
 extern "C" {
 #endif
 
-#define BASED_ABI_VERSION 2
+/* Raised whenever an entry point is added or changed; 3 added based_device_info. */
+#define BASED_ABI_VERSION 3
 
 typedef enum {
     BASED_OK = 0,

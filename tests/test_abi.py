@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.lib()
     for name in header_symbols():
         assert hasattr(lib, name), name
-    assert lib.based_abi_version() == 2
+    assert lib.based_abi_version() == 3
     for s in range(6):
         assert lib.based_status_string(s)
     assert lib.based_kernel_name(0) == b"based_segment_state_kernel"
