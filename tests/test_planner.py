@@ -51,3 +51,13 @@ def test_forced_segment_length_rounds_to_chunks():
     assert plan(1, 1000, 2, 16, 64, 100)[:2] == (8, 128)
     assert plan(1, 1000, 2, 16, 128, 100)[:2] == (8, 128)
     assert plan(1, 1000, 2, 16, 64, 5000)[:2] == (1, 1024)
+
+
+def test_too_many_work_items_rejected():
+    """The kernels number their work items in 32 bits: a shape with 2^30 (b, h) pairs is refused on the
+    host (status 2, unsupported) instead of launching an oversized grid."""
+    from taylor_feature_map_amd import _lib
+    with pytest.raises(_lib.BasedError) as e:
+        plan(1 << 20, 64, 1 << 10, 16, 64)
+    assert e.value.status == _lib.BASED_ERR_UNSUPPORTED
+    assert plan(1 << 12, 64, 1 << 10, 16, 64)[0] == 1  # 2^22 pairs, one segment: fine
