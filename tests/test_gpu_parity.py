@@ -56,6 +56,11 @@ def _gate(o, ref, what):
     (2, 1000, 2, 16, 192, None, torch.bfloat16),
     (1, 700, 1, 8, 128, 0.35, torch.float32),
     (1, 300, 2, 16, 512, None, torch.float32),     # widest V: four 128-column items per head
+    # XCD-affine block order (the (b, h, columns) pairs split over the XCDs in whole cache lines):
+    (4, 1000, 8, 16, 192, None, torch.bfloat16),   # three 64-column items per head, 6 paired segments
+    (4, 700, 16, 8, 64, None, torch.float32),      # 3 segments (odd: no pairing)
+    (2, 1500, 16, 16, 128, None, torch.bfloat16),  # 128-column items, state sums written in two halves
+    (8, 300, 32, 8, 128, None, torch.bfloat16),    # the items fill every CU: one segment
 ])
 def test_parity_full(B, T, H, K, V, scale, out):
     qb, kb, vb = make_qkv(B, T, H, K, V, seed=T + 7 * K + V)
