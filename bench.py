@@ -149,7 +149,7 @@ def _blas_name():
         return None
 
 
-def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3):
+def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3, cpu_budget_s=10.0):
     import torch
 
     from taylor_feature_map_amd import Timer, based_forward, plan
@@ -276,7 +276,7 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3
         "device": device_info(props),
     }
     if with_cpu:
-        result["cpu_baseline"] = cpu_baseline(w, qb, kb, vb)
+        result["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, cpu_budget_s)
     return result
 
 
@@ -412,6 +412,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all", action="store_true", help="also print a line per workload to stderr")
+    ap.add_argument("--oracle-all", action="store_true",
+                    help="with --all, also time the oracle (3 s sample) on every workload")
     ap.add_argument("--page-shapes", action="store_true",
                     help="also print a line per measure and grader shape of the page to stderr")
     ap.add_argument("--decode", default=None, metavar="B,H,K,V[;B,H,K,V...]",
@@ -439,11 +441,14 @@ def main():
         # every workload, then the headline shape again with fp32 output as a secondary row
         extra = dataclasses.replace(head, name=head.name + "_f32out", out_dtype="f32")
         for w in list(WORKLOADS) + [extra]:
-            r = run_bench(w, a.steps, a.warmup, with_cpu=False, settle_s=a.settle_ms / 1e3)
-            log(json.dumps({"workload": w.name, "ms_per_step": r["ms_per_step"],
-                            "cold_ms": r["ms_per_step_cold_median"], "tokens_per_s": r["value"],
-                            "tflops": r["tflops_canonical"], "path_hbm_frac": r["path_hbm_frac"],
-                            "kernels": r["kernels"]}))
+            r = run_bench(w, a.steps, a.warmup, with_cpu=a.oracle_all, settle_s=a.settle_ms / 1e3, cpu_budget_s=3.0)
+            line = {"workload": w.name, "ms_per_step": r["ms_per_step"], "cold_ms": r["ms_per_step_cold_median"],
+                    "tokens_per_s": r["value"], "tflops": r["tflops_canonical"],
+                    "path_hbm_frac": r["path_hbm_frac"], "kernels": r["kernels"]}
+            if "cpu_baseline" in r:
+                line["oracle_tokens_per_s"] = r["cpu_baseline"]["value"]
+                line["oracle_gflops"] = r["cpu_baseline"]["canonical_gflops"]
+            log(json.dumps(line))
     if a.page_shapes:
         from taylor_feature_map_amd.inputs import PAGE_SHAPES
         for w in PAGE_SHAPES:
