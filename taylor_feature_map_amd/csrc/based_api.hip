@@ -55,6 +55,12 @@ based_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V
 Plan make_plan(const Shape& sh, int64_t seg_override) {
   Plan pl;
   pl.item_cols = based::item_columns(sh.V);
+  if (pl.item_cols == 128 && sh.K == 16 && seg_override == 0) {
+    // 128-column items too few to give every CU one, 64-column items enough: the halves recompute the
+    // features, but one segment without a state pass is faster (3-6.5% on such shapes).
+    const int64_t pairs128 = sh.B * sh.H * (sh.V / 128);
+    if (pairs128 < kCUs && 2 * pairs128 >= kCUs) pl.item_cols = 64;
+  }
   pl.nvs = sh.V / pl.item_cols;
   const int64_t ck = based::chunk_tokens(sh.K, pl.item_cols);
   const int64_t t_round = (sh.T + ck - 1) / ck * ck;

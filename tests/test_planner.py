@@ -9,8 +9,13 @@ from hypothesis import assume, given, settings, strategies as st  # noqa: E402
 from taylor_feature_map_amd import plan  # noqa: E402
 
 
-def chunk(K, V):
-    return 128 if (K == 16 and V % 128 == 0) else 64
+def chunk(K, V, B, H):
+    # 128-column items (128-token chunks for K = 16) unless 64-column items would fill every CU in one
+    # segment while 128-column ones could not
+    if K == 16 and V % 128 == 0:
+        pairs128 = B * H * V // 128
+        return 64 if 128 <= pairs128 < 256 else 128
+    return 64
 
 
 @settings(max_examples=300, deadline=None)
@@ -19,7 +24,7 @@ def chunk(K, V):
 def test_plan_invariants(B, T, H, K, V):
     assume(T * H * V * 4 <= 2 ** 31 - 1)  # the library's 32-bit row ranges
     G, L, ws = plan(B, T, H, K, V)
-    C = chunk(K, V)
+    C = chunk(K, V, B, H)
     assert L % C == 0 and L >= C
     assert G == -(-T // L) and (G - 1) * L < T <= G * L
     assert G <= 8 or L >= 256, "more than eight segments shorter than 256 tokens"
@@ -41,6 +46,9 @@ def test_plan_invariants(B, T, H, K, V):
     ((8, 16384, 32, 16, 64), 1, 16384),   # the items alone fill every CU: no state pass
     ((8, 16384, 32, 8, 128), 1, 16384),
     ((16, 2048, 16, 16, 64), 1, 2048),
+    ((8, 4096, 16, 16, 128), 1, 4096),    # 64-column items fill every CU where 128-column ones would not
+    ((8, 8192, 32, 16, 128), 1, 8192),    # 128-column items already fill every CU
+    ((2, 16384, 32, 16, 128), 4, 4096),   # too few for either: 128-column items, 4 segments
     ((1, 65000, 16, 16, 64), 32, 2048),   # long sequence: scanned segment sums
 ])
 def test_measured_plans(shape, G, L):
