@@ -52,31 +52,23 @@ based_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V
   return BASED_OK;
 }
 
-Plan make_plan(const Shape& sh, int64_t seg_override) {
-  Plan pl;
-  pl.item_cols = based::item_columns(sh.V);
-  if (pl.item_cols == 128 && sh.K == 16 && seg_override == 0) {
-    // 128-column items too few to give every CU one, 64-column items enough: the halves recompute the
-    // features, but one segment without a state pass is faster (3-6.5% on such shapes).
-    const int64_t pairs128 = sh.B * sh.H * (sh.V / 128);
-    if (pairs128 < kCUs && 2 * pairs128 >= kCUs) pl.item_cols = 64;
-  }
-  pl.nvs = sh.V / pl.item_cols;
-  const int64_t ck = based::chunk_tokens(sh.K, pl.item_cols);
+// Segment length for items of `item_cols` columns (see make_plan).
+int64_t segment_length(const Shape& sh, int64_t item_cols, int64_t seg_override) {
+  const int64_t ck = based::chunk_tokens(sh.K, item_cols);
   const int64_t t_round = (sh.T + ck - 1) / ck * ck;
   int64_t L;
   if (seg_override > 0) {
     L = (seg_override + ck - 1) / ck * ck;
   } else {
-    const int64_t pairs = sh.B * sh.H * pl.nvs;
-    const int64_t waves = pairs * based::waves_per_item(sh.K, pl.item_cols);
+    const int64_t pairs = sh.B * sh.H * (sh.V / item_cols);
+    const int64_t waves = pairs * based::waves_per_item(sh.K, item_cols);
     if (pairs >= kCUs && waves >= kTargetWaves / 2) {
       // The (b, h, columns) items alone give every CU a workgroup and every SIMD a wave: one segment, no
       // state pass (a second wave per SIMD gains less than the state pass over half the keys costs).
       L = t_round;
     } else {
       // Two waves per SIMD, except K = 8 with 128 columns, whose read-out is closest to memory-bound: one.
-      const int64_t target = (sh.K == 8 && pl.item_cols == 128) ? kTargetWaves / 2 : kTargetWaves;
+      const int64_t target = (sh.K == 8 && item_cols == 128) ? kTargetWaves / 2 : kTargetWaves;
       const int64_t g_target = (target + waves - 1) / waves;
       L = (sh.T + g_target - 1) / g_target;
       L = (L + ck - 1) / ck * ck;
@@ -87,7 +79,24 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
     if (L < l_min) L = l_min;
     if (L < kShortSegment && (sh.T + L - 1) / L > kMaxShortSegments) L = (kShortSegment + ck - 1) / ck * ck;
   }
-  if (L > t_round) L = t_round;
+  return L > t_round ? t_round : L;
+}
+
+Plan make_plan(const Shape& sh, int64_t seg_override) {
+  Plan pl;
+  pl.item_cols = based::item_columns(sh.V);
+  if (pl.item_cols == 128 && sh.K == 16 && seg_override == 0) {
+    // 64-column items instead when 128-column ones leave CUs idle and 64-column ones do not, or when only
+    // 64-column items avoid the state pass: the halves recompute phi and the scores, which costs less
+    // (measured 3-7% faster where the state pass goes, 24-28% on short sequences; 18% slower where both
+    // widths fill the CUs with the same segments).
+    const int64_t p128 = sh.B * sh.H * (sh.V / 128), p64 = 2 * p128;
+    const int64_t g128 = (sh.T + segment_length(sh, 128, 0) - 1) / segment_length(sh, 128, 0);
+    const int64_t g64 = (sh.T + segment_length(sh, 64, 0) - 1) / segment_length(sh, 64, 0);
+    if ((p128 * g128 < kCUs && p64 * g64 >= kCUs) || (g128 > 1 && g64 == 1)) pl.item_cols = 64;
+  }
+  pl.nvs = sh.V / pl.item_cols;
+  const int64_t L = segment_length(sh, pl.item_cols, seg_override);
   pl.seg_len = L;
   pl.segments = (sh.T + L - 1) / L;
   pl.slot_floats = based::state_slot_floats(sh.K, pl.item_cols);

@@ -9,13 +9,14 @@ from hypothesis import assume, given, settings, strategies as st  # noqa: E402
 from taylor_feature_map_amd import plan  # noqa: E402
 
 
-def chunk(K, V, B, H):
-    # 128-column items (128-token chunks for K = 16) unless 64-column items would fill every CU in one
-    # segment while 128-column ones could not
-    if K == 16 and V % 128 == 0:
-        pairs128 = B * H * V // 128
-        return 64 if 128 <= pairs128 < 256 else 128
-    return 64
+def slot_floats(K, cols):
+    # fp32 words of one segment sum: per feature tile, the value tiles' 64 lanes x 4 rows, plus the ones
+    # tile's 16 (10 tiles for K = 16, 3 for K = 8)
+    return (10 if K == 16 else 3) * ((cols // 16) * 4 * 64 + 16)
+
+
+def chunk(K, cols):
+    return 128 if (K == 16 and cols == 128) else 64
 
 
 @settings(max_examples=300, deadline=None)
@@ -24,13 +25,19 @@ def chunk(K, V, B, H):
 def test_plan_invariants(B, T, H, K, V):
     assume(T * H * V * 4 <= 2 ** 31 - 1)  # the library's 32-bit row ranges
     G, L, ws = plan(B, T, H, K, V)
-    C = chunk(K, V, B, H)
-    assert L % C == 0 and L >= C
+    assert L % 64 == 0 and L >= 64
     assert G == -(-T // L) and (G - 1) * L < T <= G * L
     assert G <= 8 or L >= 256, "more than eight segments shorter than 256 tokens"
-    if G > 1:
-        assert L >= (2 if K == 16 else 1) * C
     assert (ws == 0) == (G == 1)
+    if G > 1:
+        # the workspace holds one sum per (b, h, item, segment but the last): it tells the item width
+        widths = [c for c in ((128, 64) if V % 128 == 0 else (64,))
+                  if ws == B * H * (V // c) * (G - 1) * slot_floats(K, c) * 4]
+        assert len(widths) == 1, (ws, widths)
+        C = chunk(K, widths[0])
+        assert L % C == 0 and L >= (2 if K == 16 else 1) * C
+        if K == 8 or V % 128 != 0:
+            assert widths[0] == (128 if V % 128 == 0 else 64)
 
 
 @pytest.mark.parametrize("shape,G,L", [
@@ -47,6 +54,7 @@ def test_plan_invariants(B, T, H, K, V):
     ((8, 16384, 32, 8, 128), 1, 16384),
     ((16, 2048, 16, 16, 64), 1, 2048),
     ((8, 4096, 16, 16, 128), 1, 4096),    # 64-column items fill every CU where 128-column ones would not
+    ((1, 2048, 16, 16, 128), 8, 256),     # short sequence: 64-column items (all CUs) over 128-column (half)
     ((8, 8192, 32, 16, 128), 1, 8192),    # 128-column items already fill every CU
     ((2, 16384, 32, 16, 128), 4, 4096),   # too few for either: 128-column items, 4 segments
     ((1, 65000, 16, 16, 64), 32, 2048),   # long sequence: scanned segment sums
