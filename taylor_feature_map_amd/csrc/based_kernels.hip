@@ -811,7 +811,9 @@ __device__ __forceinline__ void intra_step(const Stage<Cf>& st, int ks, const u3
 // tile and value columns 16 vt + 4 g .. 16 vt + 4 g + 3, so each value tile is one 8-byte (bf16) or
 // 16-byte (fp32) store per lane; the ones tile holds den in all four rows. voff is the lane's byte
 // offset of (token c, column 4 g); the tile's first token goes into the scalar offset. Rows past the end
-// of the sequence fall outside the output buffer range and are dropped.
+// of the sequence fall outside the output buffer range and are dropped. A 16-byte store still reads its
+// data registers after it issues, and with the offset in an SGPR the compiler lets the next tile's
+// products overwrite them at once: the build inserts the wait states (hazard_pad.py).
 template <class Cf, bool OUT_F32>
 __device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned voff, unsigned soff,
                                            const f32x4_t (&O)[Cf::NVT]) {
