@@ -45,29 +45,29 @@ def algorithmic_bytes(B, T, H, K, V, out_bytes):
     return B * T * H * (4 * K + 2 * V) + B * T * H * V * out_bytes
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "taylor_feature_map_amd", "csrc", "based_kernels.hip")
+LIB_FILE = os.path.join(ROOT, "taylor_feature_map_amd", "libbased.so")
 
 
 def traffic_file(workload_name):
     return os.path.join(ROOT, "profiles", f"based_chunk_readout_traffic_{workload_name}.md")
 
 
-def kernel_code_digest(path=KERNEL_SOURCE):
-    """SHA-256 of the kernel source with comments and blank lines left out, so that the digest changes
-    when the code does and not when a comment does."""
+def device_code_digest(lib=LIB_FILE):
+    """SHA-256 of the gfx950 code object inside the built library, or None without one. It changes
+    whenever the device code does (kernel source, compiler flags, the build's store padding) and not for
+    comments or host code; rebuilding the same sources gives the same bytes."""
     import hashlib
-    import re
-    lines = []
-    for line in open(path):
-        code = re.sub(r"//.*", "", line).strip()
-        if code:
-            lines.append(code)
-    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+    from taylor_feature_map_amd.hazard_pad import code_objects
+    if not os.path.exists(lib):
+        return None
+    with open(lib, "rb") as f:
+        co = code_objects(f.read()).get("hipv4-amdgcn-amd-amdhsa--gfx950")
+    return hashlib.sha256(co).hexdigest() if co else None
 
 
 def measured_traffic(workload_name):
     """HBM bytes per read-out launch from the committed rocprofv3 summary of this workload, or None when
-    there is none or it was taken on different kernel code."""
+    there is none or it was taken on different device code."""
     path = traffic_file(workload_name)
     if not os.path.exists(path):
         return None
@@ -76,7 +76,8 @@ def measured_traffic(workload_name):
         if ":" in line and line.startswith("    "):
             key, val = line.strip().split(":", 1)
             fields[key.strip()] = val.strip()
-    if fields.get("kernel_code_sha256") != kernel_code_digest():
+    digest = device_code_digest()
+    if digest is None or fields.get("device_code_sha256") != digest:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
