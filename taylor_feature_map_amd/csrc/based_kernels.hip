@@ -185,10 +185,17 @@ struct Feat<8> {
   template <int T, int R>
   __device__ static __forceinline__ float qval(const QSide& y, int g) {
     const bool h0 = g < 2;
+    // Both candidates of a tile are formed before the select: written as a choice between two array
+    // elements, the compiler folds it into one load at an offset that depends on g and keeps the query
+    // arrays in scratch memory.
     if constexpr (T == 0) {
-      return h0 ? y.h[R] * y.u[R] : y.a[R] * y.u[(R - 1) & 7];
+      const float p0 = y.h[R] * y.u[R];
+      const float p1 = y.a[R] * y.u[(R - 1) & 7];
+      return h0 ? p0 : p1;
     } else if constexpr (T == 1) {
-      return y.a[R] * y.u[(R - (h0 ? 2 : 3)) & 7];
+      const float p2 = y.a[R] * y.u[(R - 2) & 7];
+      const float p3 = y.a[R] * y.u[(R - 3) & 7];
+      return h0 ? p2 : p3;
     } else if constexpr (T == 2) {
       const float p = y.a[R] * y.u[(R - 4) & 7];
       return h0 ? ((g & 1) == 0 ? p : (R == 0 ? 1.0f : 0.0f)) : y.l[R];

@@ -115,3 +115,29 @@ def test_built_library_obeys_the_rule(tmp_path):
     # the same listing without its s_nop lines breaks the rule: the checker reads this disassembly
     stripped = "\n".join(x for x in dis.split("\n") if not ((i := hp.parse_instruction(x)) and i.opcode == "s_nop"))
     assert len(hp.check(stripped)) > 10
+
+
+READELF = "/opt/rocm/lib/llvm/bin/llvm-readelf"
+
+
+@pytest.mark.skipif(not (os.path.exists(LIB) and shutil.which(READELF)), reason="library or llvm-readelf missing")
+def test_no_kernel_uses_scratch(tmp_path):
+    """Every kernel keeps its values in registers and LDS: no private segment and no spills. (A query-side
+    choice between two array elements once put the K = 8 read-out's arrays in scratch memory, stored and
+    reloaded every chunk.)"""
+    with open(LIB, "rb") as f:
+        co = hp.code_objects(f.read())["hipv4-amdgcn-amd-amdhsa--gfx950"]
+    path = tmp_path / "kernels.hsaco"
+    path.write_bytes(co)
+    notes = subprocess.run([READELF, "--notes", str(path)], capture_output=True, text=True, check=True).stdout
+    kernels, fields = [], {}
+    for line in notes.split("\n"):
+        s = line.strip()
+        if s.startswith(".name:"):
+            kernels.append(s.split(":", 1)[1].strip())
+        for key in ("private_segment_fixed_size", "sgpr_spill_count", "vgpr_spill_count"):
+            if s.startswith(f".{key}:"):
+                fields.setdefault(key, []).append(int(s.split(":", 1)[1]))
+    assert len(kernels) >= 10
+    for key, vals in fields.items():
+        assert len(vals) == len(kernels) and all(v == 0 for v in vals), (key, list(zip(kernels, vals)))
