@@ -77,7 +77,14 @@ int64_t segment_length(const Shape& sh, int64_t item_cols, int64_t seg_override)
     // larger, so that each further segment costs more start-up reads (measured on short sequences).
     const int64_t l_min = (sh.K == 16 ? 2 : 1) * ck;
     if (L < l_min) L = l_min;
-    if (L < kShortSegment && (sh.T + L - 1) / L > kMaxShortSegments) L = (kShortSegment + ck - 1) / ck * ck;
+    // Segments shorter than kShortSegment tokens only up to kMaxShortSegments of them: beyond that, the
+    // shortest length that gives that many (at most kShortSegment).
+    if (L < kShortSegment && (sh.T + L - 1) / L > kMaxShortSegments) {
+      const int64_t l8 = (sh.T + kMaxShortSegments - 1) / kMaxShortSegments;
+      L = (l8 + ck - 1) / ck * ck;
+      const int64_t l_short = (kShortSegment + ck - 1) / ck * ck;
+      if (L > l_short) L = l_short;
+    }
   }
   return L > t_round ? t_round : L;
 }

@@ -45,6 +45,8 @@ def test_plan_invariants(B, T, H, K, V):
     ((2, 512, 8, 16, 64), 4, 128),        # short K = 16 sequence: two chunks per segment
     ((1, 256, 4, 16, 128), 1, 256),       # two 128-token chunks: one kernel
     ((1, 4096, 16, 8, 128), 16, 256),     # at most eight segments shorter than 256 tokens
+    ((1, 1024, 8, 8, 64), 8, 128),        # ... and then eight of the shortest length (18% faster than 4 x 256)
+    ((1, 1536, 4, 8, 128), 8, 192),       # (9% faster than 6 x 256)
     ((2, 2048, 8, 16, 64), 8, 256),
     ((4, 8192, 16, 16, 64), 8, 1024),     # two waves per SIMD
     ((4, 8192, 16, 8, 64), 16, 512),      # K = 8 with 64 columns: two waves per SIMD as well
