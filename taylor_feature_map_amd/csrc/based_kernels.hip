@@ -83,7 +83,7 @@ __device__ __forceinline__ float ror(float x) {
     return x;
   } else {
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + D, 0xf, 0xf, false));
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + D, 0xf, 0xf, true));
   }
 }
 
