@@ -108,9 +108,15 @@ def parse_instruction(text: str) -> Optional[Instr]:
     return Instr(opcode, _split_operands(rest), waits)
 
 
+_LABEL = re.compile(r"^[A-Za-z_.$][\w.$]*:\s*$")          # assembly: a symbol at the start of the line
+_DIS_LABEL = re.compile(r"^[0-9a-fA-F]+ <[^>]+>:\s*$")     # llvm-objdump: address <symbol>:
+
+
 def is_label(text: str) -> bool:
-    s = text.split(";")[0].strip()
-    return s.endswith(":")
+    """A label line of assembly or disassembly (never an indented line, such as a YAML key in the
+    metadata block)."""
+    s = text.split(";")[0].rstrip()
+    return bool(_LABEL.match(s) or _DIS_LABEL.match(s))
 
 
 class _Tracker:

@@ -74,6 +74,12 @@ def test_labels_and_branches_drain():
     assert rep.drains == 2 and hp.check(out) == [] and hp.same_program(src, out)
 
 
+def test_labels_are_only_symbols_at_line_start():
+    assert hp.is_label(".LBB0_12:") and hp.is_label("_ZN5based3fooEv:   ; @_ZN5based3fooEv")
+    assert hp.is_label("0000000000001900 <_ZN5based3fooEv>:")
+    assert not hp.is_label("  - .args:") and not hp.is_label("      .name:           foo") and not hp.is_label("\ts_nop 0")
+
+
 def test_same_program_rejects_any_other_change():
     src = _asm(STORE, "\tv_mul_f32_e32 v61, v65, v74")
     out = hp.pad(src).lines
