@@ -53,16 +53,11 @@ def traffic_file(workload_name):
 
 
 def device_code_digest(lib=LIB_FILE):
-    """SHA-256 of the gfx950 code object inside the built library, or None without one. It changes
-    whenever the device code does (kernel source, compiler flags, the build's store padding) and not for
-    comments or host code; rebuilding the same sources gives the same bytes."""
-    import hashlib
-    from taylor_feature_map_amd.hazard_pad import code_objects
-    if not os.path.exists(lib):
-        return None
-    with open(lib, "rb") as f:
-        co = code_objects(f.read()).get("hipv4-amdgcn-amd-amdhsa--gfx950")
-    return hashlib.sha256(co).hexdigest() if co else None
+    """SHA-256 of the instruction bytes of the gfx950 code object inside the built library, or None
+    without one. It changes whenever the device code does (kernel source, compiler flags) and not for
+    comments, host code or the directory the library was built in."""
+    from taylor_feature_map_amd.codeobj import text_digest
+    return text_digest(lib)
 
 
 def measured_traffic(workload_name):

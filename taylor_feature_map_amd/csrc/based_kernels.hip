@@ -817,10 +817,10 @@ __device__ __forceinline__ void intra_step(const Stage<Cf>& st, int ks, const u3
 // o = num / (den + 1e-6) for one 16-token query tile held transposed: lane (c, g) has token c of the
 // tile and value columns 16 vt + 4 g .. 16 vt + 4 g + 3, so each value tile is one 8-byte (bf16) or
 // 16-byte (fp32) store per lane; the ones tile holds den in all four rows. voff is the lane's byte
-// offset of (token c, column 4 g); the tile's first token goes into the scalar offset. Rows past the end
-// of the sequence fall outside the output buffer range and are dropped. A 16-byte store still reads its
-// data registers after it issues, and with the offset in an SGPR the compiler lets the next tile's
-// products overwrite them at once: the build inserts the wait states (hazard_pad.py).
+// offset of (token c, column 4 g), soff the tile's first token. Rows past the end of the sequence fall
+// outside the output buffer range and are dropped. A store of more than 8 bytes reads its data registers
+// after it issues; the compiler keeps a later write of them far enough behind only when the store's
+// scalar offset is a constant, so the 16-byte fp32 stores carry the whole offset in the vector offset.
 template <class Cf, bool OUT_F32>
 __device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned voff, unsigned soff,
                                            const f32x4_t (&O)[Cf::NVT]) {
@@ -829,7 +829,7 @@ __device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned v
   for (int vt = 0; vt < Cf::NVV; ++vt) {
     if constexpr (OUT_F32) {
       const f32x4_t o = O[vt] * inv;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, voff, soff + 64 * vt, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, voff + soff + 64 * vt, 0, 0);
     } else {
       const u32x2_t o = {pack2(O[vt][0] * inv, O[vt][1] * inv), pack2(O[vt][2] * inv, O[vt][3] * inv)};
       __builtin_amdgcn_raw_buffer_store_b64(o, ro, voff, soff + 32 * vt, 0);
