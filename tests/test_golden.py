@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 from oracle import based_ref_chunked, based_ref_direct, based_ref_rational
+from oracle.based_direct_c import based_ref_direct_c
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 FILES = sorted(glob.glob(os.path.join(GOLDEN, "*.txt")))
@@ -35,6 +36,15 @@ def load(path):
     return q, k, v, scale, o
 
 
+def bf16_bits(x):
+    """bf16 bit patterns of values that bf16 holds exactly (the fixtures' inputs)."""
+    f = np.asarray(x, dtype=np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(x, dtype=np.float64))
+    u = f.view(np.uint32)
+    assert np.all(u & 0xFFFF == 0), "value not exact in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
 def test_fixtures_present():
     assert len(FILES) >= 3
 
@@ -52,5 +62,10 @@ def test_oracle_reproduces_worked_example(path):
     for route in (based_ref_direct(q, k, v, float(scale)),
                   based_ref_chunked(q, k, v, float(scale), chunk=1),
                   based_ref_chunked(q, k, v, float(scale), chunk=2),
-                  based_ref_chunked(q, k, v, float(scale), chunk=T)):
+                  based_ref_chunked(q, k, v, float(scale), chunk=T),
+                  based_ref_direct_c(bf16_bits(q), bf16_bits(k), bf16_bits(v), float(scale))):
         np.testing.assert_allclose(route, want, rtol=1e-14, atol=1e-15)
+    # the C route evaluates any chosen rows on their own
+    rows = np.arange(T)[::-1]
+    np.testing.assert_allclose(based_ref_direct_c(bf16_bits(q), bf16_bits(k), bf16_bits(v), float(scale), rows),
+                               want[:, rows], rtol=1e-14, atol=1e-15)

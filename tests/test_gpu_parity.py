@@ -1,10 +1,10 @@
 """GPU parity of the HIP causal Based forward against the CPU oracle (run on an MI355X).
 
 Gate (max-abs 2e-2 and relative-L2 5e-3 over the compared elements) as stated for bf16 inputs against the
-float32-or-better oracle. Small shapes are compared element by element over the whole output; the full
-benchmark shapes are compared on sampled rows that the oracle evaluates one by one from the definition
-(spec_md of the page "Write a fast Based (Taylor linear attention) forward kernel"), plus properties
-that hold at any size.
+float32-or-better oracle. Shapes are compared element by element over the whole output (the benchmark
+configurations at full size are in test_gpu_benchmark_configs.py); the longest sequence the buffer ranges
+allow is compared on sampled rows that the oracle evaluates one by one from the definition (spec_md of the
+page "Write a fast Based (Taylor linear attention) forward kernel").
 """
 import numpy as np
 import pytest
@@ -46,8 +46,8 @@ def _gate(o, ref, what):
 # ------------------------------------------------------------------ small shapes, full comparison
 
 @pytest.mark.parametrize("B,T,H,K,V,scale,out", [
-    (1, 512, 2, 8, 64, None, torch.float32),      # smallest benchmark shape
-    (2, 2048, 8, 16, 64, None, torch.bfloat16),   # second benchmark shape
+    (1, 512, 2, 8, 64, None, torch.float32),      # smallest benchmark shape, another seed
+    (2, 2048, 8, 16, 64, None, torch.bfloat16),   # second benchmark shape, another seed
     (1, 1, 1, 16, 64, None, torch.bfloat16),
     (2, 31, 3, 16, 64, 0.2, torch.float32),
     (1, 33, 2, 8, 128, -0.3, torch.bfloat16),
@@ -155,40 +155,7 @@ def test_constant_values_and_zero_scale():
     _gate(o, np.cumsum(v, axis=1) / (t + 1 + 1e-6), "scale 0 running mean")
 
 
-# ------------------------------------------------------------------ the benchmark shapes at full size
-
-def _sample_rows(T, seg_len, rng, n_random=40):
-    rows = {0, 1, 2, 15, 16, 31, 32, 33, T - 1, T - 2, T - 33}
-    for s in range(seg_len, T, seg_len):
-        rows |= {s - 1, s, s + 1}
-    rows |= set(rng.integers(0, T, n_random).tolist())
-    return sorted(r for r in rows if 0 <= r < T)
-
-
-@pytest.mark.parametrize("wi", [2, 3, 4])
-def test_parity_benchmark_shapes_sampled(wi):
-    from taylor_feature_map_amd import plan
-    w = WORKLOADS[wi]
-    qb, kb, vb = make_qkv(w.B, w.T, w.H, w.K, w.V, w.seed)
-    out = torch.float32 if w.out_dtype == "f32" else torch.bfloat16
-    o = _run(qb, kb, vb, w.scale, out)
-    assert o.shape == (w.B, w.T, w.H, w.V)
-    assert np.all(np.isfinite(o))
-    # Convex-combination bound: every output channel lies within the running range of |v| (bf16 slack).
-    vabs = np.abs(bf16_to_f64(vb))
-    bound = np.maximum.accumulate(vabs, axis=1)
-    assert np.all(np.abs(o) <= bound * (1 + 2 ** -7) + 1e-6)
-    _, seg_len, _ = plan(w.B, w.T, w.H, w.K, w.V)
-    rng = np.random.default_rng(wi)
-    got, want = [], []
-    pairs = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2), (0, w.H - 1)]
-    for b, h in pairs:
-        rows = _sample_rows(w.T, seg_len, rng)
-        want.append(based_ref_direct_rows(bf16_to_f64(qb[b:b + 1]), bf16_to_f64(kb[b:b + 1]),
-                                          bf16_to_f64(vb[b:b + 1]), w.scale, 0, h, rows))
-        got.append(o[b, rows, h, :])
-    _gate(np.concatenate(got), np.concatenate(want), f"{w.name} sampled rows")
-
+# ------------------------------------------------------------------ the longest sequence
 
 def test_parity_maximum_row_range():
     """The largest sequence the 32-bit buffer ranges allow at H = 1, V = 64 with fp32 output:

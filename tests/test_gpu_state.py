@@ -165,8 +165,8 @@ def test_decode_steps_many_value_blocks(K, V):
 
 def test_decode_step_at_benchmark_batch():
     """The decode step at the batch the bench times (B = 64, H = 16, K = 16, V = 64: 1024 workgroups), from
-    the state of a 4-token prefix, checked on sampled (b, h) pairs against the oracle's step on those pairs,
-    and every output finite."""
+    the state of a 4-token prefix, checked on every (b, h) pair against the oracle's step: the outputs and
+    the updated state and normaliser."""
     from taylor_feature_map_amd import based_decode_step
     B, H, K, V, T0 = 64, 16, 16, 64, 4
     qb, kb, vb = make_qkv(B, T0 + 1, H, K, V, seed=4242)
@@ -175,20 +175,7 @@ def test_decode_step_at_benchmark_batch():
     state = (_f32(st[0]), _f32(st[1]))
     o = based_decode_step(_to_dev(qb[:, T0]), _to_dev(kb[:, T0]), _to_dev(vb[:, T0]), state, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    o = _np(o)
-    assert np.all(np.isfinite(o))
-    rng = np.random.default_rng(5)
-    pairs = [(0, 0), (B - 1, H - 1)] + [tuple(x) for x in zip(rng.integers(0, B, 6), rng.integers(0, H, 6))]
-    S_dev, z_dev = _np(state[0]), _np(state[1])
-    got, want, s_got, s_want, z_got, z_want = [], [], [], [], [], []
-    for b, h in pairs:
-        st_bh = (st[0][b:b + 1, h:h + 1], st[1][b:b + 1, h:h + 1])
-        o_ref, st_new = based_ref_decode_step(q[b:b + 1, T0, h:h + 1], k[b:b + 1, T0, h:h + 1],
-                                              v[b:b + 1, T0, h:h + 1], st_bh, None)
-        got.append(o[b, h]); want.append(o_ref[0, 0])
-        s_got.append(S_dev[b, h]); s_want.append(st_new[0][0, 0])
-        z_got.append(z_dev[b, h]); z_want.append(st_new[1][0, 0])
-    print(f"decode B{B} H{H}: {len(pairs)} sampled pairs", flush=True)
-    _gate(np.stack(got), np.stack(want), "decode step at the benchmark batch")
-    _state_gate((np.stack(s_got), np.stack(z_got)), (np.stack(s_want), np.stack(z_want)),
-                "decode state at the benchmark batch")
+    o_ref, st_new = based_ref_decode_step(q[:, T0], k[:, T0], v[:, T0], st, None)
+    print(f"decode B{B} H{H}: all {B * H} pairs", flush=True)
+    _gate(_np(o), o_ref, "decode step at the benchmark batch")
+    _state_gate((_np(state[0]), _np(state[1])), st_new, "decode state at the benchmark batch")

@@ -12,6 +12,7 @@ hypothesis = pytest.importorskip("hypothesis")
 from hypothesis import given, settings, strategies as st  # noqa: E402
 
 from oracle import based_ref_chunked, based_ref_direct, based_ref_rational, rational_to_f64  # noqa: E402
+from oracle.based_direct_c import based_ref_direct_c  # noqa: E402
 
 
 def _bf16(x):
@@ -54,3 +55,32 @@ def test_float_routes_match_exact_rationals(prob):
     exact = rational_to_f64(based_ref_rational(q, k, v, scale))
     np.testing.assert_allclose(based_ref_direct(q, k, v, scale), exact, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(based_ref_chunked(q, k, v, scale, chunk=2), exact, rtol=1e-12, atol=1e-14)
+
+
+def _bits(x):
+    """bf16 bit patterns of float64 values that are bf16 already."""
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@settings(max_examples=40, deadline=None)
+@given(problems(max_t=300, max_k=16, max_v=70), st.data())
+def test_c_definition_equals_numpy_definition(prob, data):
+    """The plain-C route (the definition's loops, float64) and the numpy route agree to rounding, on all rows
+    and on any chosen subset of rows."""
+    q, k, v, scale = prob
+    d = based_ref_direct(q, k, v, scale)
+    c = based_ref_direct_c(_bits(q), _bits(k), _bits(v), scale)
+    np.testing.assert_allclose(c, d, rtol=1e-11, atol=1e-13)
+    T = q.shape[1]
+    rows = np.array(data.draw(st.lists(st.integers(0, T - 1), min_size=1, max_size=8)), dtype=np.int64)
+    cr = based_ref_direct_c(_bits(q), _bits(k), _bits(v), scale, rows)
+    np.testing.assert_allclose(cr, d[:, rows], rtol=1e-11, atol=1e-13)
+
+
+@settings(max_examples=20, deadline=None)
+@given(problems(max_t=6, max_k=3, max_v=2))
+def test_c_definition_matches_exact_rationals(prob):
+    q, k, v, scale = prob
+    exact = rational_to_f64(based_ref_rational(q, k, v, scale))
+    np.testing.assert_allclose(based_ref_direct_c(_bits(q), _bits(k), _bits(v), scale), exact, rtol=1e-12,
+                               atol=1e-14)
