@@ -27,8 +27,10 @@
  * Execution: asynchronous on `stream` (no device synchronisation); launch errors are returned as
  * BASED_ERR_HIP, faults inside a kernel surface at the caller's next synchronisation. Argument errors
  * are detected on the host before any HIP call is made, and nothing is enqueued in that case.
- * Thread safety: all entry points are re-entrant and keep no global state (a timer object must not be
- * shared between threads). Calls that share a workspace buffer must be ordered on one stream.
+ * Thread safety: all entry points are re-entrant (a timer object must not be shared between threads).
+ * The only global state is based_forward_noalloc's static scratch and its per-device address, looked up
+ * under a mutex. Calls that share a workspace buffer, or that use the static scratch on one device, must
+ * be ordered (e.g. on one stream).
  * Determinism: for a given device and shape, the reduction order is fixed, so results are bitwise
  * repeatable.
  */
@@ -44,8 +46,8 @@
 extern "C" {
 #endif
 
-/* Raised whenever an entry point is added or changed; 3 added based_device_info. */
-#define BASED_ABI_VERSION 3
+/* Raised whenever an entry point is added or changed; 3 added based_device_info, 4 based_forward_noalloc. */
+#define BASED_ABI_VERSION 4
 
 typedef enum {
     BASED_OK = 0,
@@ -92,6 +94,26 @@ based_status_t based_forward_ws(const void* q, const void* k, const void* v,
                                 int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                 float scale, void* out, based_dtype_t out_dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * based_forward for callers that cannot allocate device memory: code recorded under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same operation and arguments as based_forward;
+ * no allocation of any kind is made (no hipMalloc, hipMallocAsync or library allocation). The workspace
+ * is a static device array of the library, based_noalloc_scratch_bytes() bytes (32 MiB) on every device
+ * the library runs on, held until the process ends; its device address is looked up on the first call on
+ * a device (the device of `stream`) and kept.
+ *   Errors: as based_forward; BASED_ERR_UNSUPPORTED when the shape's plan needs more workspace than the
+ *   static scratch holds (no shape of the automatic plans does up to now: they need at most ~21 MiB).
+ * Every call on one device shares that device's scratch (the segment state sums are fully written before
+ * they are read, so nothing carries over from an earlier call): calls that overlap in time on one
+ * device, such as calls on two streams without ordering between them, race and give wrong results.
+ */
+based_status_t based_forward_noalloc(const void* q, const void* k, const void* v,
+                                     int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                                     float scale, void* out, based_dtype_t out_dtype, hipStream_t stream);
+
+/* Bytes of the static scratch of based_forward_noalloc. */
+size_t based_noalloc_scratch_bytes(void);
 
 /* ---------------------------------------------------------------------------------------------------
  * State on either side of the forward: carried in and out, and the one-token recurrent step.

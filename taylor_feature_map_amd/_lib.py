@@ -26,6 +26,9 @@ SIGNATURES = {
     "based_forward_workspace_bytes": (ctypes.c_size_t, [_i64] * 5),
     "based_forward": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp,
                                      ctypes.c_int, _vp]),
+    "based_forward_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp,
+                                             ctypes.c_int, _vp]),
+    "based_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "based_forward_ws": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, ctypes.c_float, _vp,
                                         ctypes.c_int, _vp, ctypes.c_size_t, _vp]),
     "based_forward_plan": (ctypes.c_int, [_i64] * 6 + [ctypes.POINTER(_i64), ctypes.POINTER(_i64),

@@ -149,9 +149,14 @@ struct based_timer {
 
 namespace {
 
+// Where the workspace comes from: the caller (ws, ws_bytes), stream-ordered allocation, or the library's
+// static device scratch.
+enum class Workspace { kCaller, kAllocate, kScratch };
+
 based_status_t run(const void* q, const void* k, const void* v, const Shape& sh, float scale, void* out,
                    based_dtype_t out_dtype, void* ws, size_t ws_bytes, int64_t seg_override, based_timer* timer,
-                   hipStream_t stream, bool allocate, const based::StateIO& io = based::StateIO{}) {
+                   hipStream_t stream, Workspace wsk, const based::StateIO& io = based::StateIO{}) {
+  const bool allocate = wsk == Workspace::kAllocate;
   if (based_status_t s = check_shape(sh.B, sh.T, sh.H, sh.K, sh.V)) return s;
   if (!q || !k || !v || !out) return fail(BASED_ERR_INVALID_ARGUMENT, "null tensor pointer");
   if (out_dtype != BASED_BF16 && out_dtype != BASED_F32)
@@ -196,7 +201,12 @@ based_status_t run(const void* q, const void* k, const void* v, const Shape& sh,
   const Plan pl = make_plan(sh, seg_override);
   if (based_status_t s = check_items(sh, pl)) return s;
   const size_t need = workspace_bytes(sh, pl);
-  if (!allocate) {
+  if (wsk == Workspace::kScratch) {
+    if (need > based::kScratchBytes)
+      return fail(BASED_ERR_UNSUPPORTED, "the plan needs " + std::to_string(need) +
+                                             " bytes of workspace, more than the static scratch's " +
+                                             std::to_string(based::kScratchBytes));
+  } else if (!allocate) {
     if (need > 0 && !ws) return fail(BASED_ERR_WORKSPACE_TOO_SMALL, "workspace required but NULL");
     if (ws_bytes < need)
       return fail(BASED_ERR_WORKSPACE_TOO_SMALL,
@@ -213,6 +223,12 @@ based_status_t run(const void* q, const void* k, const void* v, const Shape& sh,
   const bool out_f32 = out_dtype == BASED_F32;
 
   float* wsf = static_cast<float*>(ws);
+  if (wsk == Workspace::kScratch && need > 0) {
+    void* p = nullptr;
+    const hipError_t e = based::scratch_buffer(stream, &p);
+    if (e != hipSuccess) return fail(BASED_ERR_HIP, std::string("static scratch: ") + hipGetErrorString(e));
+    wsf = static_cast<float*>(p);
+  }
   if (allocate && need > 0) {
     void* p = nullptr;
     const hipError_t e = hipMallocAsync(&p, need, stream);
@@ -292,14 +308,24 @@ based_status_t based_forward_plan(int64_t B, int64_t T, int64_t H, int64_t K, in
 based_status_t based_forward(const void* q, const void* k, const void* v, int64_t B, int64_t T, int64_t H,
                              int64_t K, int64_t V, float scale, void* out, based_dtype_t out_dtype,
                              hipStream_t stream) {
-  return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, nullptr, 0, 0, nullptr, stream, true);
+  return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, nullptr, 0, 0, nullptr, stream,
+             Workspace::kAllocate);
 }
+
+based_status_t based_forward_noalloc(const void* q, const void* k, const void* v, int64_t B, int64_t T, int64_t H,
+                                     int64_t K, int64_t V, float scale, void* out, based_dtype_t out_dtype,
+                                     hipStream_t stream) {
+  return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, nullptr, 0, 0, nullptr, stream,
+             Workspace::kScratch);
+}
+
+size_t based_noalloc_scratch_bytes(void) { return based::kScratchBytes; }
 
 based_status_t based_forward_ws(const void* q, const void* k, const void* v, int64_t B, int64_t T, int64_t H,
                                 int64_t K, int64_t V, float scale, void* out, based_dtype_t out_dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, workspace, workspace_bytes, 0, nullptr, stream,
-             false);
+             Workspace::kCaller);
 }
 
 based_status_t based_forward_ex(const void* q, const void* k, const void* v, int64_t B, int64_t T, int64_t H,
@@ -307,7 +333,7 @@ based_status_t based_forward_ex(const void* q, const void* k, const void* v, int
                                 void* workspace, size_t workspace_bytes, int64_t segment_len_override,
                                 based_timer* timer, hipStream_t stream) {
   return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, workspace, workspace_bytes, segment_len_override,
-             timer, stream, false);
+             timer, stream, Workspace::kCaller);
 }
 
 int64_t based_feature_dim(int64_t K) { return 1 + K + K * K; }
@@ -318,7 +344,7 @@ based_status_t based_forward_state(const void* q, const void* k, const void* v, 
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const based::StateIO io{state_in, norm_in, state_out, norm_out};
   return run(q, k, v, Shape{B, T, H, K, V}, scale, out, out_dtype, workspace, workspace_bytes, 0, nullptr, stream,
-             workspace == nullptr, io);
+             workspace == nullptr ? Workspace::kAllocate : Workspace::kCaller, io);
 }
 
 based_status_t based_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t K,

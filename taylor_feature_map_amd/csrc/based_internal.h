@@ -67,4 +67,11 @@ hipError_t launch_kernel(int kernel_id, const void* q, const void* k, const void
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t K,
                               int64_t V, float sigma, float* S, float* z, void* out, bool out_f32, hipStream_t stream);
 
+// Bytes of the static device scratch that based_forward_noalloc uses as its workspace.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+
+// Device address of that scratch on the device that `stream` belongs to, looked up once per device and
+// kept. No allocation is made.
+hipError_t scratch_buffer(hipStream_t stream, void** ptr);
+
 }  // namespace based

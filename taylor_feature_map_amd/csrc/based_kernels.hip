@@ -52,6 +52,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "based_internal.h"
 
 namespace based {
@@ -1271,6 +1273,40 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, int64
                        static_cast<const u16*>(k), static_cast<const u16*>(v), V, sigma, S, z, out, out_f32);
   }
   return hipGetLastError();
+}
+
+// Workspace of based_forward_noalloc, for callers that cannot allocate: one copy per device, held until
+// the process ends. Host code never names it directly (in host code the name is a stand-in, not a device
+// address): scratch_buffer() looks up the device address once per device and hands that out.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t scratch_buffer(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (r != hipSuccess) return r;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 int item_columns(int64_t V) { return V % 128 == 0 ? 128 : 64; }

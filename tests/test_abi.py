@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.lib()
     for name in header_symbols():
         assert hasattr(lib, name), name
-    assert lib.based_abi_version() == 3
+    assert lib.based_abi_version() == 4
     for s in range(6):
         assert lib.based_status_string(s)
     assert lib.based_kernel_name(0) == b"based_segment_state_kernel"
@@ -141,3 +141,33 @@ def call_decode(q=FAKE, state=S_IN, norm=Z_IN, K=16, V=64, out=0x80000000, scale
 ])
 def test_decode_step_rejects_bad_arguments(kw, status):
     assert call_decode(**kw) == status
+
+
+def test_noalloc_entry_point_validates_on_the_host():
+    """based_forward_noalloc takes based_forward's arguments and rejects bad ones before any HIP call."""
+    lib = _lib.lib()
+    assert lib.based_noalloc_scratch_bytes() == 32 << 20
+    for kw, status in ((dict(q=0), _lib.BASED_ERR_INVALID_ARGUMENT), (dict(B=0), _lib.BASED_ERR_INVALID_ARGUMENT),
+                       (dict(K=12), _lib.BASED_ERR_UNSUPPORTED), (dict(scale=math.inf), _lib.BASED_ERR_INVALID_ARGUMENT),
+                       (dict(out=FAKE), _lib.BASED_ERR_INVALID_ARGUMENT)):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, B=1, T=64, H=2, K=16, V=64, scale=math.nan, out=0x80000000, dt=0)
+        a.update(kw)
+        got = lib.based_forward_noalloc(a["q"], a["k"], a["v"], a["B"], a["T"], a["H"], a["K"], a["V"], a["scale"],
+                                        a["out"], a["dt"], None)
+        assert got == status, (kw, got)
+
+
+def test_automatic_plans_fit_the_static_scratch():
+    """The workspace of every automatic plan over a grid of shapes stays within the static scratch of
+    based_forward_noalloc (the largest needs about 21 MiB)."""
+    lib = _lib.lib()
+    cap = lib.based_noalloc_scratch_bytes()
+    worst = 0
+    for K in (8, 16):
+        for V in (64, 128, 256, 512):
+            for B, H in ((1, 1), (1, 2), (1, 16), (2, 8), (4, 16), (8, 32), (16, 64)):
+                for T in (64, 300, 1024, 4096, 16384, 65000, 131072, 1 << 20):
+                    if T * H * V * 4 > 2 ** 31 - 1:
+                        continue
+                    worst = max(worst, lib.based_forward_workspace_bytes(B, T, H, K, V))
+    assert 0 < worst <= cap
