@@ -145,7 +145,35 @@ def _blas_name():
         return None
 
 
-def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3, cpu_budget_s=10.0):
+SWEEP_BYTES = 1 << 30  # read before every cold step: 4x the 256 MB Infinity Cache, 256x the L2
+
+
+def counter_summary(workload_name):
+    """MFMA-busy figures of the read-out kernel from the committed rocprofv3 counter summary of this
+    workload, or None when there is none or it was taken on different device code."""
+    path = os.path.join(ROOT, "profiles", f"based_kernels_{workload_name}_counters.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("    "):
+            key, val = line.strip().split(":", 1)
+            fields[key.strip()] = val.strip()
+    digest = device_code_digest()
+    if digest is None or fields.get("device_code_sha256") != digest or "readout_mfma_busy_frac" not in fields:
+        return None
+    return {"readout_mfma_busy_frac": float(fields["readout_mfma_busy_frac"]),
+            "readout_valu_insts_per_token_head": float(fields.get("readout_valu_insts_per_token_head", "nan"))}
+
+
+def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3, cpu_budget_s=10.0, cold_steps=10):
+    """Times the whole forward on workload w.
+
+    Warm: `steps` back-to-back steps after the clocks have settled (the throughput), the same again with
+    HIP events around every kernel (their average durations), and single steps between events. Cold:
+    before each of `cold_steps` steps a read of a 1 GiB buffer (a sum) evicts L2 and the Infinity Cache, so
+    the step reads its inputs from HBM; the read leaves no dirty lines behind to drain inside the step.
+    Cold steps are timed once between events and once with events around every kernel."""
     import torch
 
     from taylor_feature_map_amd import Timer, based_forward, plan
@@ -164,10 +192,18 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3
     out = torch.empty((w.B, w.T, w.H, w.V), dtype=out_dtype, device=dev)
     segments, seg_len, ws_bytes = plan(w.B, w.T, w.H, w.K, w.V)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    timer = Timer(max_launches=3 * steps + 16)  # events around every kernel of a step
+    timer = Timer(max_launches=3 * max(steps, cold_steps) + 16)  # events around every kernel of a step
 
     def step(t=None):
         based_forward(q, k, v, w.scale, out=out, workspace=ws, timer=t)
+
+    def kernel_times(t):
+        res = {}
+        for kid in Timer.KERNELS:
+            n, ms = t.read(kid)
+            if n:
+                res[Timer.kernel_name(kid)] = {"launches": n, "avg_us": ms * 1e3 / n}
+        return res
 
     # Settle: untimed back-to-back steps for at least settle_s seconds before the warm-up steps. The GPU
     # needs tens of milliseconds of continuous work to reach its loaded clocks (the first ~30 ms of a
@@ -192,8 +228,7 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3
     ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
 
     # The same K steps again with HIP events recorded on the launch stream around every kernel (events at
-    # kernel boundaries cost a few microseconds each, so the throughput above is taken without them): the
-    # average duration of each kernel, the dominant one giving the roofline figure.
+    # kernel boundaries cost a few microseconds each, so the throughput above is taken without them).
     timer.reset()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -201,45 +236,49 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3
         step(timer)
     torch.cuda.synchronize()
     ms_instrumented = (time.perf_counter() - t1) * 1e3 / steps
-    per_kernel = {}
-    for kid in Timer.KERNELS:
-        n, ms = timer.read(kid)
-        if n:
-            per_kernel[Timer.kernel_name(kid)] = {"launches": n, "avg_us": ms * 1e3 / n}
-    n_dom, ms_dom = timer.read(Timer.READOUT)
-    dom_us = ms_dom * 1e3 / n_dom
+    warm_kernels = kernel_times(timer)
 
-    # Single steps, each bracketed by HIP events on the launch stream: median and minimum.
-    single = []
-    for _ in range(steps):
+    # Single warm steps, each bracketed by HIP events on the launch stream: median and minimum.
+    def bracketed(before=None):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        if before is not None:
+            before()
         e0.record()
         step()
         e1.record()
         torch.cuda.synchronize()
-        single.append(e0.elapsed_time(e1))
+        return e0.elapsed_time(e1)
 
-    # Cold-cache steps: a 512 MiB write between steps evicts L2 and the Infinity Cache.
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-    cold = []
-    for _ in range(min(steps, 10)):
-        flush.zero_()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        step()
-        e1.record()
+    single = [bracketed() for _ in range(steps)]
+
+    # Cold steps: a read-only sweep of 1 GiB before each one.
+    sweep = torch.ones(SWEEP_BYTES // 4, dtype=torch.float32, device=dev)
+    evict = lambda: sweep.sum()  # noqa: E731
+    cold = [bracketed(evict) for _ in range(cold_steps)]
+    timer.reset()
+    for _ in range(cold_steps):
+        evict()
+        step(timer)
         torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    del flush
+    cold_kernels = kernel_times(timer)
+    del sweep
 
     out_bytes = 4 if w.out_dtype == "f32" else 2
     flops = canonical_flops(w.B, w.T, w.H, w.K, w.V)
     nbytes = algorithmic_bytes(w.B, w.T, w.H, w.K, w.V, out_bytes)
     tokens = w.B * w.T
     dom = "based_chunk_readout_kernel"
-    achieved = nbytes / (dom_us * 1e-6) / 1e9
+    cold_us = cold_kernels[dom]["avg_us"]
+    warm_us = warm_kernels[dom]["avg_us"]
+    cold_med = float(np.median(cold))
+
+    def roof(us):
+        achieved = nbytes / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name), "kernel": dom,
+                "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": us}
+
     result = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
@@ -257,23 +296,38 @@ def run_bench(w, steps, warmup, with_cpu=True, device_inputs=False, settle_s=0.3
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
                    "scale": w.scale, "out_dtype": w.out_dtype, "seed": w.seed,
                    "segments": segments, "segment_len": seg_len},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name), "kernel": dom,
-                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": dom_us},
+        "roofline": dict(roof(cold_us), cache="cold"),
+        "roofline_warm": dict(roof(warm_us), cache="warm"),
         "tflops_canonical": flops / (ms_per_step * 1e-3) / 1e12,
         "path_hbm_frac": nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "path_hbm_frac_cold": nbytes / (cold_med * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "path_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "ms_per_step_with_kernel_events": ms_instrumented,
         "ms_per_step_single_median": float(np.median(single)),
         "ms_per_step_single_min": float(np.min(single)),
-        "ms_per_step_cold_median": float(np.median(cold)) if cold else None,
-        "ms_per_step_cold_min": float(np.min(cold)) if cold else None,
-        "kernels": per_kernel,
+        "ms_per_step_cold_median": cold_med,
+        "ms_per_step_cold_min": float(np.min(cold)),
+        "kernels": warm_kernels,
+        "kernels_cold": cold_kernels,
+        "counters": counter_summary(w.name),
         "device": device_info(props),
     }
     if with_cpu:
         result["cpu_baseline"] = cpu_baseline(w, qb, kb, vb, cpu_budget_s)
     return result
+
+
+def config_summary(r):
+    """The per-configuration figures carried in the main JSON line."""
+    c = r["config"]
+    return {"workload": c["workload"], "segments": c["segments"], "ms_per_step": r["ms_per_step"],
+            "ms_per_step_cold": r["ms_per_step_cold_median"], "tokens_per_s": r["value"],
+            "tflops_canonical": r["tflops_canonical"], "path_hbm_frac": r["path_hbm_frac"],
+            "path_hbm_frac_cold": r["path_hbm_frac_cold"], "readout_us_cold": r["roofline"]["avg_launch_us"],
+            "readout_hbm_frac_cold": r["roofline"]["frac"], "readout_us_warm": r["roofline_warm"]["avg_launch_us"],
+            "readout_hbm_frac_warm": r["roofline_warm"]["frac"], "traffic": r["roofline"]["traffic"],
+            "counters": r["counters"],
+            "kernels_cold_us": {k: round(v["avg_us"], 3) for k, v in r["kernels_cold"].items()}}
 
 
 def device_info(props):
@@ -398,6 +452,31 @@ def copy_probe(mib, reps):
     print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": reps}))
 
 
+def row_probe(B, T, H, reps):
+    """Reads a (B, T, H, 16) bf16 tensor as the read-out kernel reads q and k: one workgroup per (b, h),
+    32-byte rows at a stride of H * 32 bytes, 16-byte loads, heads that share a 128-byte line on one XCD.
+    Every byte is read once per launch, so profiler counters taken on it give the factor between counter
+    readings and bytes read for this access pattern."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "taylor_feature_map_amd", "libbased_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.based_probe_read_rows.restype = ctypes.c_int
+    lib.based_probe_read_rows.argtypes = [ctypes.c_void_p] + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2
+    dev = torch.device("cuda:0")
+    x = torch.ones((B, T, H, 16), dtype=torch.bfloat16, device=dev)
+    sink = torch.empty(B * H * 64, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        rc = lib.based_probe_read_rows(x.data_ptr(), B, T, H, sink.data_ptr(), stream)
+        if rc != 0:
+            raise SystemExit(f"based_probe_read_rows failed: {rc}")
+    torch.cuda.synchronize()
+    print(json.dumps({"row_probe_bytes_read": B * T * H * 32, "launches": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,6 +486,8 @@ def main():
                     help="untimed back-to-back steps for at least this long before the warm-up steps")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="measure the selected workload only (the JSON line then has no other configurations)")
     ap.add_argument("--all", action="store_true", help="also print a line per workload to stderr")
     ap.add_argument("--oracle-all", action="store_true",
                     help="with --all, also time the oracle (3 s sample) on every workload")
@@ -418,6 +499,8 @@ def main():
                     help="also print the forward with state in and out against the plain forward (stderr)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--row-probe", default=None, metavar="B,T,H",
+                    help="only run the 32-byte-row read probe over a (B,T,H,16) bf16 tensor (counter calibration)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this implementation has no multi-GPU path "
@@ -427,24 +510,34 @@ def main():
     if a.copy_probe_mib > 0:
         copy_probe(a.copy_probe_mib, a.steps)
         return
+    if a.row_probe:
+        row_probe(*(int(x) for x in a.row_probe.split(",")), a.steps)
+        return
     if a.steps < 1 or a.warmup < 0:
         raise SystemExit("--steps must be >= 1 and --warmup >= 0")
+    from taylor_feature_map_amd.inputs import WORKLOADS
+    w_main = pick_workload(a.workload)
+    # Every benchmark configuration is measured (warm and cold) and summarised in the JSON line; the main
+    # workload's figures are the line's own. --all adds the headline shape with fp32 output on stderr.
+    summaries, main_res = [], None
+    for w in ([w_main] if a.only else WORKLOADS):
+        r = run_bench(w, a.steps, a.warmup, with_cpu=(w == w_main and not a.no_cpu_baseline) or a.oracle_all,
+                      settle_s=a.settle_ms / 1e3, cpu_budget_s=10.0 if w == w_main else 3.0)
+        summaries.append(config_summary(r))
+        if "cpu_baseline" in r and w != w_main:
+            summaries[-1]["oracle_tokens_per_s"] = r["cpu_baseline"]["value"]
+        if a.all:
+            log(json.dumps(summaries[-1]))
+        if w == w_main:
+            main_res = r
+    if main_res is None:
+        main_res = run_bench(w_main, a.steps, a.warmup, with_cpu=not a.no_cpu_baseline, settle_s=a.settle_ms / 1e3)
     if a.all:
         import dataclasses
-
-        from taylor_feature_map_amd.inputs import WORKLOADS
         head = pick_workload(None)
-        # every workload, then the headline shape again with fp32 output as a secondary row
         extra = dataclasses.replace(head, name=head.name + "_f32out", out_dtype="f32")
-        for w in list(WORKLOADS) + [extra]:
-            r = run_bench(w, a.steps, a.warmup, with_cpu=a.oracle_all, settle_s=a.settle_ms / 1e3, cpu_budget_s=3.0)
-            line = {"workload": w.name, "ms_per_step": r["ms_per_step"], "cold_ms": r["ms_per_step_cold_median"],
-                    "tokens_per_s": r["value"], "tflops": r["tflops_canonical"],
-                    "path_hbm_frac": r["path_hbm_frac"], "kernels": r["kernels"]}
-            if "cpu_baseline" in r:
-                line["oracle_tokens_per_s"] = r["cpu_baseline"]["value"]
-                line["oracle_gflops"] = r["cpu_baseline"]["canonical_gflops"]
-            log(json.dumps(line))
+        log(json.dumps(config_summary(run_bench(extra, a.steps, a.warmup, with_cpu=False,
+                                                settle_s=a.settle_ms / 1e3))))
     if a.page_shapes:
         from taylor_feature_map_amd.inputs import PAGE_SHAPES
         for w in PAGE_SHAPES:
@@ -464,9 +557,8 @@ def main():
             log(json.dumps(decode_bench(B, H, K, V, max(a.steps, 100), a.settle_ms / 1e3)))
     if a.with_state:
         log(json.dumps(state_forward_bench(pick_workload(a.workload), a.steps, a.settle_ms / 1e3)))
-    w = pick_workload(a.workload)
-    res = run_bench(w, a.steps, a.warmup, with_cpu=not a.no_cpu_baseline, settle_s=a.settle_ms / 1e3)
-    print(json.dumps(res), flush=True)
+    main_res["configs"] = summaries
+    print(json.dumps(main_res), flush=True)
 
 
 if __name__ == "__main__":

@@ -15,6 +15,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libbased.so")
+# A measurement probe kept out of the product library (bench.py --row-probe).
+PROBE = "probe_read.hip"
+PROBE_LIB = os.path.join(PKG, "libbased_probe.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 KERNELS = "based_kernels.hip"
 API = "based_api.hip"
@@ -56,8 +59,12 @@ def build(verbose: bool = False) -> str:
                    "-o", p("based_kernels.o")], verbose)
     api = _start([HIPCC, *DEVICE, *COMMON, "-cuid=based_api", "-fPIC", "-c", os.path.join(CSRC, API),
                   "-o", p("based_api.o")], verbose)
+    probe = _start([HIPCC, *DEVICE, *COMMON, "-cuid=probe_read", "-fPIC", "-shared", os.path.join(CSRC, PROBE),
+                    "-o", PROBE_LIB + ".tmp"], verbose)
     _finish(kern, "kernels compile")
     _finish(api, "api compile")
+    _finish(probe, "probe build")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     tmp = LIB + ".tmp"
     _finish(_start([HIPCC, f"--offload-arch={ARCH}", "-fPIC", "-shared", p("based_kernels.o"), p("based_api.o"),
                     "-o", tmp], verbose), "link")

@@ -51,3 +51,22 @@ def test_oracle_baseline_leg():
     assert np.isfinite(r["value"]) and r["value"] > 0
     # at least one (b, h) sequence, and more than one pass over the two pairs in 0.2 s of oracle time
     assert "(b,h) sequences of T=96" in r["sample"]
+
+
+def test_counter_figures_only_for_the_built_code():
+    assert bench.counter_summary("no_such_workload") is None
+
+
+def test_row_probe_argument_check():
+    """The 32-byte-row read probe (counter calibration) refuses a (b, h) count that does not split over the
+    8 XCDs, on the host."""
+    import ctypes
+    path = os.path.join(ROOT, "taylor_feature_map_amd", "libbased_probe.so")
+    if not os.path.exists(path):
+        import pytest
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(path)
+    lib.based_probe_read_rows.restype = ctypes.c_int
+    lib.based_probe_read_rows.argtypes = [ctypes.c_void_p] + [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 2
+    assert lib.based_probe_read_rows(0x10000, 1, 64, 3, 0x20000, None) == 1
+    assert lib.based_probe_read_rows(None, 1, 64, 8, 0x20000, None) == 1
