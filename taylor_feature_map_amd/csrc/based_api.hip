@@ -112,6 +112,11 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
   // heads covers whole 128-byte lines of the q and k rows (64 / K heads per line).
   const int64_t pairs = sh.B * sh.H * pl.nvs, ppx = pairs / 8, line_heads = 64 / sh.K;
   pl.affine = pairs % 8 == 0 && (ppx % sh.H == 0 || (sh.H % line_heads == 0 && ppx % line_heads == 0));
+  // Output rows written whole (through LDS) rather than as 16-row tiles: measured 21% faster read-out at
+  // K = 8 with 128 columns and 2-7% at K = 16 with 64 columns when segments share the CUs, 6% slower with
+  // a single segment (one workgroup per CU, where the extra LDS round trip is not hidden). The K = 16,
+  // 128-column read-out has no registers to spare for it and never does it.
+  pl.row_stores = sh.K == 8 || (pl.item_cols == 64 && pl.segments > 1);
   return pl;
 }
 

@@ -23,6 +23,7 @@ struct Plan {
   int64_t segments, seg_len, nvs, item_cols, slot_floats;
   bool scanned;
   bool affine;  // XCD-affine work items (every segment of a (b, h, columns) pair on one XCD)
+  bool row_stores;  // bf16 output tiles staged through LDS and stored as whole rows
 };
 
 // Upper bound on the work items (blocks) of one launch; below it all item index arithmetic fits in 32 bits.

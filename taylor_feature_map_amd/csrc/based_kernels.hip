@@ -607,6 +607,9 @@ struct StateSplit {
   static constexpr int FW = W / KW;
   static constexpr int NT = Feat<Cf::K>::NPT / FW;
   static constexpr int KS = Split<Cf>::NKS / KW;  // key steps per wave and chunk
+  // Chunks loaded ahead of the one being worked on: with K = 8 there is less work per chunk to cover the
+  // latency of the loads (measured: 3 sets are 18% faster than 1 at K = 8, V = 128; no change at K = 16).
+  static constexpr int PREFETCH = Cf::K == 8 ? 3 : 2;
   static_assert(NT * FW == Feat<Cf::K>::NPT && KS * KW == Split<Cf>::NKS, "even split");
 };
 
@@ -636,26 +639,45 @@ __device__ __forceinline__ void segment_state_body(StateSmem<SC>& sm, const Rows
 #pragma unroll
     for (int vt = 0; vt < SC::NVT; ++vt) S[t][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // As in the read-out: chunk c + 1 is loaded at the top of iteration c and staged at its end.
-  Prefetch<SC, false, WI> pf;
-  pf.init(rw, lane);
-  pf.load(rw, t_begin);
-  pf.store(sm.stage[0], lane);
-  int it = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += SP::C, ++it) {
-    const Stage<SC>& st = sm.stage[it & 1];
-    pf.load(rw, t0 + SP::C < t_end ? t0 + SP::C : T);  // past the range after the last chunk: no traffic
-    __syncthreads();
+  // The loop does little work per chunk next to the latency of a global load, so the inputs are loaded
+  // D = SS::PREFETCH chunks ahead into as many register sets (two LDS stages as in the read-out): chunk
+  // c + 1 is staged at the end of iteration c from the set loaded D - 1 iterations before, and that set is
+  // then refilled with chunk c + 1 + D. Loads past the segment read the
+  // next segment's rows (or, past the sequence, nothing) and are never used.
+  constexpr int D = SS::PREFETCH;
+  Prefetch<SC, false, WI> pf[D];
+  pf[0].init(rw, lane);
 #pragma unroll
-    for (int j = 0; j < SS::KS; ++j) {
-      const int ks = KG * SS::KS + j;
-      u32x4_t vop[SC::NVT];
-      load_value_operands<SC>(st, ks, lane, vop);
-      float kx[8];
-      key_column<SC>(st, ks, lane, kx);
-      state_update_step<SC, T0, NT>(S, kx, vop, c);
-    }
-    pf.store(sm.stage[(it + 1) & 1], lane);  // read in iteration c - 1, finished before this iteration's barrier
+  for (int d = 1; d < D; ++d) pf[d] = pf[0];
+  auto at = [&](int64_t t) { return t < t_end ? t : T; };  // past the sequence: no traffic
+  pf[0].load(rw, t_begin);
+  pf[0].store(sm.stage[0], lane);
+#pragma unroll
+  for (int d = 0; d < D; ++d) pf[d].load(rw, at(t_begin + (d + 1) * SP::C));
+  int it = 0;
+  int64_t t0 = t_begin;
+  bool more = true;
+  while (more) {
+    constexpr_for<0, D>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      if (!more) return;
+      const Stage<SC>& st = sm.stage[it & 1];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < SS::KS; ++j) {
+        const int ks = KG * SS::KS + j;
+        u32x4_t vop[SC::NVT];
+        load_value_operands<SC>(st, ks, lane, vop);
+        float kx[8];
+        key_column<SC>(st, ks, lane, kx);
+        state_update_step<SC, T0, NT>(S, kx, vop, c);
+      }
+      pf[d].store(sm.stage[(it + 1) & 1], lane);  // read in iteration c - 1, finished before this iteration's barrier
+      pf[d].load(rw, at(t0 + (D + 1) * SP::C));
+      t0 += SP::C;
+      ++it;
+      more = t0 < t_end;
+    });
   }
   __syncthreads();  // the stages are free: their memory holds the partial sums now
   if constexpr (KG == 1) {
@@ -839,6 +861,53 @@ __device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned v
   }
 }
 
+// bf16 output tile II of wave WI written as whole rows, in two steps. The tile (16 tokens, VS columns)
+// first goes into LDS, into 1 KiB blocks of the idle stage that this wave alone refills with the next
+// chunk at the end of the iteration: wave WI's prefetch units WI * 64 + i * 64 W .. + 63 occupy bytes
+// 1024 (WI + W i) .. + 1023 of a stage, and no wave reads that stage before the next barrier, so no barrier
+// is needed (a wave's own LDS accesses are carried out in order). A block holds RB = 1024 / (2 VS) rows of
+// the tile in plain row order, so that every address is one lane base plus a constant (a swizzle against
+// the bank conflicts of the 8-byte writes would cost a live address register per value tile, more than
+// the conflicts cost). Later, once the registers of the chunk's contraction are free, the rows are read
+// back as UPR 16-byte units each and stored with one 128-bit store per lane, so every store instruction
+// covers RB whole rows of the output (32 bytes of each of 16 rows in the register layout otherwise).
+template <class Cf, int WI, int II>
+struct TileRows {
+  static constexpr int W = Split<Cf>::W;
+  static constexpr int VS = Cf::VS;
+  static constexpr int UPR = VS / 8;          // 16-byte units per row
+  static constexpr int RB = 1024 / (2 * VS);  // rows per 1 KiB block
+  static constexpr int NB = 16 / RB;          // blocks per tile
+  static_assert((WI + W * (NB * (II + 1) - 1)) * 64 < Units<Cf>::NU, "the tile's blocks lie inside the wave's prefetch units");
+  __device__ static __forceinline__ unsigned char* block(unsigned char* idle_stage, int j) {
+    return idle_stage + 1024 * (WI + W * (NB * II + j));
+  }
+  // o = num / (den + 1e-6) as bf16 into the blocks.
+  __device__ static __forceinline__ void stage(unsigned char* idle_stage, const f32x4_t (&O)[Cf::NVT], int lane) {
+    const int c = lane & 15, g = lane >> 4;
+    const float inv = __builtin_amdgcn_rcpf(O[Cf::ONES][0] + 1e-6f);
+    unsigned char* rowp = block(idle_stage, c / RB) + (c % RB) * (2 * VS) + 8 * (g & 1);
+#pragma unroll
+    for (int vt = 0; vt < Cf::NVV; ++vt) {
+      const u32x2_t o = {pack2(O[vt][0] * inv, O[vt][1] * inv), pack2(O[vt][2] * inv, O[vt][3] * inv)};
+      const int u = 2 * vt + (g >> 1);
+      *reinterpret_cast<u32x2_t*>(rowp + 16 * (u ^ (c & (UPR - 1)))) = o;
+    }
+  }
+  // The rows to the output; soff is the byte offset of the tile's first token. As for every store of more
+  // than 8 bytes, the whole offset goes in the vector offset (the scalar offset is the constant 0).
+  __device__ static __forceinline__ void store(unsigned char* idle_stage, __amdgpu_buffer_rsrc_t ro,
+                                               unsigned out_stride, unsigned soff, int lane) {
+    const int r = lane / UPR, p = lane % UPR;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int row = j * RB + r;
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(block(idle_stage, j) + r * (2 * VS) + 16 * (p ^ (row & (UPR - 1))));
+      __builtin_amdgcn_raw_buffer_store_b128(x, ro, r * out_stride + 16 * p + soff + j * RB * out_stride, 0, 0);
+    }
+  }
+};
+
 // The state at the start of a segment: the sum, in segment order, of the state sums of the `n_src`
 // earlier segments stored at src, src + slot_floats, ...
 template <class Cf, int T0, int NT, typename SA>
@@ -936,13 +1005,15 @@ __device__ __forceinline__ void export_state(const SA& S, const StateView& sv, f
   }
 }
 
-template <class Cf, int WI, bool OUT_F32>
+template <class Cf, int WI, bool OUT_F32, bool ROWS>
 __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw, __amdgpu_buffer_rsrc_t ro,
                                              unsigned out_stride, int64_t T, int64_t t_begin, int64_t t_end,
                                              float c1, float c2, float sigma, const float* __restrict__ src,
                                              int64_t n_src, int64_t slot_floats, const StateView& sv) {
   constexpr int K = Cf::K;
   constexpr int NVT = Cf::NVT;
+  // Whole-row output stores exist for bf16 output; K = 16 with 128 columns has no registers to spare for them.
+  static_assert(!ROWS || (!OUT_F32 && !(K == 16 && Cf::VS == 128)), "no whole-row stores for this read-out");
   using F = Feat<K>;
   using SP = Split<Cf>;
   constexpr int T0 = SP::T0(WI), NT = SP::NT(WI);
@@ -1043,6 +1114,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw
     // ---- per 32-token key step: intra-chunk term (direct polynomial) for the query tiles, then fold
     //      the step into this wave's state tiles (after the last chunk the result is unused).
     const unsigned soff_out = static_cast<unsigned>(t0) * out_stride;
+    unsigned char* idle = reinterpret_cast<unsigned char*>(&sm.stage[(it + 1) & 1]);
 #pragma unroll
     for (int ks = 0; ks < SP::NKS; ++ks) {
       u32x4_t vop[NVT];
@@ -1050,14 +1122,24 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw
       constexpr_for<0, QPW>([&](auto ic) {
         constexpr int ii = decltype(ic)::value;
         intra_step<Cf, SP::Q(WI, ii)>(st, ks, vop, O[ii], c1, c2, lane);
-        if (ks == SP::NKS - 1)
-          store_tile<Cf, OUT_F32>(ro, lane_off, soff_out + 16 * SP::Q(WI, ii) * out_stride, O[ii]);
+        if (ks == SP::NKS - 1) {
+          if constexpr (ROWS)
+            TileRows<Cf, WI, ii>::stage(idle, O[ii], lane);
+          else
+            store_tile<Cf, OUT_F32>(ro, lane_off, soff_out + 16 * SP::Q(WI, ii) * out_stride, O[ii]);
+        }
       });
       if constexpr (NT > 0) {
         float kx[8];
         key_column<Cf>(st, ks, lane, kx);
         state_update_step<Cf, T0, NT>(S, kx, vop, c);
       }
+    }
+    if constexpr (ROWS) {
+      constexpr_for<0, QPW>([&](auto ic) {
+        constexpr int ii = decltype(ic)::value;
+        TileRows<Cf, WI, ii>::store(idle, ro, out_stride, soff_out + 16 * SP::Q(WI, ii) * out_stride, lane);
+      });
     }
     // The state after this chunk goes into the buffer that chunk c - 1 read (every wave finished that
     // chunk before this chunk's barrier); with a single buffer the waves first wait for each other.
@@ -1072,7 +1154,7 @@ __device__ __forceinline__ void readout_body(ReadoutSmem<Cf>& sm, const Rows& rw
 }
 
 
-template <int K, int VS, bool OUT_F32>
+template <int K, int VS, bool OUT_F32, bool ROWS>
 __global__ __launch_bounds__((Split<Cfg<K, VS>>::W * kWave)) void based_chunk_readout_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float c1,
     float c2, float sigma, const float* __restrict__ ws, void* __restrict__ out, StateIO io) {
@@ -1109,8 +1191,8 @@ __global__ __launch_bounds__((Split<Cfg<K, VS>>::W * kWave)) void based_chunk_re
   constexpr_for<0, Split<Cf>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
     if (w == WI)
-      readout_body<Cf, WI, OUT_F32>(sm, rw, ro, out_stride, sh.T, t_begin, t_end, c1, c2, sigma, src, n_src,
-                                    pl.slot_floats, sv);
+      readout_body<Cf, WI, OUT_F32, ROWS>(sm, rw, ro, out_stride, sh.T, t_begin, t_end, c1, c2, sigma, src, n_src,
+                                          pl.slot_floats, sv);
   });
 }
 
@@ -1249,12 +1331,19 @@ hipError_t launch_chunk_readout(const void* q, const void* k, const void* v, con
   const float c1 = sigma;
   const float c2 = 0.5f * sigma * sigma;
   const dim3 grid(static_cast<unsigned>(blocks)), block(Split<Cfg<K, VS>>::W * kWave);
+  constexpr bool kCanRows = !(K == 16 && VS == 128);
   if (out_f32) {
-    hipLaunchKernelGGL((based_chunk_readout_kernel<K, VS, true>), grid, block, 0, stream, static_cast<const u16*>(q),
-                       static_cast<const u16*>(k), static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out, io);
+    hipLaunchKernelGGL((based_chunk_readout_kernel<K, VS, true, false>), grid, block, 0, stream,
+                       static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v), sh, pl, c1,
+                       c2, sigma, ws, out, io);
+  } else if (kCanRows && pl.row_stores) {
+    hipLaunchKernelGGL((based_chunk_readout_kernel<K, VS, false, kCanRows>), grid, block, 0, stream,
+                       static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v), sh, pl, c1,
+                       c2, sigma, ws, out, io);
   } else {
-    hipLaunchKernelGGL((based_chunk_readout_kernel<K, VS, false>), grid, block, 0, stream, static_cast<const u16*>(q),
-                       static_cast<const u16*>(k), static_cast<const u16*>(v), sh, pl, c1, c2, sigma, ws, out, io);
+    hipLaunchKernelGGL((based_chunk_readout_kernel<K, VS, false, false>), grid, block, 0, stream,
+                       static_cast<const u16*>(q), static_cast<const u16*>(k), static_cast<const u16*>(v), sh, pl, c1,
+                       c2, sigma, ws, out, io);
   }
   return hipGetLastError();
 }
