@@ -380,10 +380,10 @@ struct Rows {
 // Chunk loader: the units of q (if WITH_Q), k and v spread over all threads of the workgroup, one
 // chunk ahead of use, through registers. Every region is a multiple of 64 units long, so the region of
 // each of wave WI's loads is known at compile time (no divergent branches around the loads).
-template <class Cf, bool WITH_Q, int WI>
+template <class Cf, bool WITH_Q, int WI, int NW = Split<Cf>::W>
 struct Prefetch {
   using U = Units<Cf>;
-  static constexpr int NTH = Split<Cf>::W * kWave;
+  static constexpr int NTH = NW * kWave;
   static constexpr int FIRST = WITH_Q ? 0 : U::NQK;  // q units are skipped without q
   static constexpr int PER = (U::NU - FIRST + NTH - 1) / NTH;
   static_assert(U::NQK % kWave == 0 && U::NV % kWave == 0, "regions must be whole waves");
@@ -594,30 +594,34 @@ __device__ __forceinline__ Rows make_rows(const u16* q, const u16* k, const u16*
 // ------------------------------------------------------------------ kernel 0: segment state sums
 
 // The state sum of a segment is split over the W waves of the workgroup two ways: FW groups of feature
-// tiles times KW groups of key steps. Wave w owns the feature tiles of group w / KW and the key steps
-// of group w % KW of every chunk, so the waves do equal MFMA work and each reads only its own key
-// steps' values from LDS; the KW partial sums of a feature group are added at the end of the segment.
-// The state kernel always works on 64 value columns (SC); with 128-column read-out items it writes each
-// half into the item's slot. K = 16: 2 x 2 (5 tiles); K = 8: 1 x 2 (3 tiles); each wave takes half the
-// chunk's key steps.
+// tiles times KW = 2 groups of key steps. Wave w owns the feature tiles of group w / KW and the key steps
+// of group w % KW of every chunk, so each wave reads only its own key steps' values from LDS; the KW partial
+// sums of a feature group are added at the end of the segment. The state kernel always works on 64 value
+// columns (SC); with 128-column read-out items it writes each half into the item's slot. K = 16: 4 x 2
+// waves, feature groups of 3, 3, 2 and 2 tiles (with 2 x 2 waves of 5 tiles, the accumulators alone took
+// 100 registers and a segment item ran 4 waves, too few to keep a CU busy: 1.75 waves per SIMD on the
+// benchmark shapes); K = 8: 1 x 2 waves of 3 tiles. Each wave takes half the chunk's key steps.
 template <class Cf>
 struct StateSplit {
-  static constexpr int W = Split<Cf>::W;
+  static constexpr bool K16 = Cf::K == 16;
   static constexpr int KW = 2;
-  static constexpr int FW = W / KW;
-  static constexpr int NT = Feat<Cf::K>::NPT / FW;
+  static constexpr int FW = K16 ? 4 : 1;
+  static constexpr int W = FW * KW;
+  __host__ __device__ static constexpr int T0(int fg) { return K16 ? (fg < 2 ? 3 * fg : 6 + 2 * (fg - 2)) : 0; }
+  __host__ __device__ static constexpr int NT(int fg) { return K16 ? (fg < 2 ? 3 : 2) : 3; }
+  static constexpr int NT_MAX = K16 ? 3 : 3;
   static constexpr int KS = Split<Cf>::NKS / KW;  // key steps per wave and chunk
   // Chunks loaded ahead of the one being worked on: with K = 8 there is less work per chunk to cover the
   // latency of the loads (measured: 3 sets are 18% faster than 1 at K = 8, V = 128; no change at K = 16).
-  static constexpr int PREFETCH = Cf::K == 8 ? 3 : 2;
-  static_assert(NT * FW == Feat<Cf::K>::NPT && KS * KW == Split<Cf>::NKS, "even split");
+  static constexpr int PREFETCH = Cf::K == 8 ? 3 : 1;
+  static_assert(T0(FW - 1) + NT(FW - 1) == Feat<Cf::K>::NPT && KS * KW == Split<Cf>::NKS, "even split");
 };
 
 template <class Cf>
 struct __align__(16) StateSmem {
   union {
     Stage<Cf> stage[2];
-    f32x4_t red[StateSplit<Cf>::FW][StateSplit<Cf>::NT][Cf::NVT][kWave];  // partial sums of key-step group 1
+    f32x4_t red[StateSplit<Cf>::FW][StateSplit<Cf>::NT_MAX][Cf::NVT][kWave];  // partial sums of key-step group 1
   };
 };
 
@@ -629,7 +633,7 @@ __device__ __forceinline__ void segment_state_body(StateSmem<SC>& sm, const Rows
   using SS = StateSplit<SC>;
   constexpr int K = SC::K;
   constexpr int FG = WI / SS::KW, KG = WI % SS::KW;
-  constexpr int T0 = FG * SS::NT, NT = SS::NT;
+  constexpr int T0 = SS::T0(FG), NT = SS::NT(FG);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int c = lane & 15;
@@ -645,7 +649,7 @@ __device__ __forceinline__ void segment_state_body(StateSmem<SC>& sm, const Rows
   // then refilled with chunk c + 1 + D. Loads past the segment read the
   // next segment's rows (or, past the sequence, nothing) and are never used.
   constexpr int D = SS::PREFETCH;
-  Prefetch<SC, false, WI> pf[D];
+  Prefetch<SC, false, WI, SS::W> pf[D];
   pf[0].init(rw, lane);
 #pragma unroll
   for (int d = 1; d < D; ++d) pf[d] = pf[0];
@@ -708,7 +712,7 @@ __device__ __forceinline__ void segment_state_body(StateSmem<SC>& sm, const Rows
 // Work items of 64 columns (pl.nvs * IVS / 64 per (b, h)); the slot belongs to the read-out item of IVS columns that
 // contains them.
 template <int K, int IVS>
-__global__ __launch_bounds__((Split<Cfg<K, 64>>::W * kWave)) void based_segment_state_kernel(
+__global__ __launch_bounds__((StateSplit<Cfg<K, 64>>::W * kWave), 2) void based_segment_state_kernel(
     const u16* __restrict__ k, const u16* __restrict__ v, Shape sh, Plan pl, float* __restrict__ ws) {
   using SC = Cfg<K, 64>;
   constexpr int HALVES = IVS / 64;
@@ -722,7 +726,7 @@ __global__ __launch_bounds__((Split<Cfg<K, 64>>::W * kWave)) void based_segment_
   const int half = static_cast<int>(ic.vs % HALVES);
   float* dst = ws + (bhv * (pl.segments - 1) + ic.g) * pl.slot_floats;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  constexpr_for<0, Split<SC>::W>([&](auto wc) {
+  constexpr_for<0, StateSplit<SC>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
     if (w == WI) segment_state_body<SC, IVS, WI>(sm, rw, sh.T, t_begin, t_end, half, dst);
   });
@@ -1308,7 +1312,7 @@ hipError_t launch_segment_state(const void* k, const void* v, const Shape& sh, c
   const int64_t items = sh.B * sh.H * (pl.nvs * VS / 64) * (pl.segments - 1);
   const int64_t blocks = (items + 7) / 8 * 8;
   hipLaunchKernelGGL((based_segment_state_kernel<K, VS>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(Split<Cfg<K, 64>>::W * kWave), 0, stream, static_cast<const u16*>(k),
+                     dim3(StateSplit<Cfg<K, 64>>::W * kWave), 0, stream, static_cast<const u16*>(k),
                      static_cast<const u16*>(v), sh, pl, ws);
   return hipGetLastError();
 }
