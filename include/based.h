@@ -77,8 +77,9 @@ size_t based_forward_workspace_bytes(int64_t B, int64_t T, int64_t H, int64_t K,
 
 /*
  * Causal Based forward (spec_md / contract_md of the page above).
- *   scale : query scale, multiplies q only, before the dot product. NaN means "None" on the page, i.e.
- *           (float)K**-0.5 (the feature dimension K, not V). +-inf is rejected.
+ *   scale : the factor on the scores s = scale * (q . k); the page applies it to the query side alone.
+ *           NaN stands for the page's default, (float)K**-0.5 with K the key width (V does not enter).
+ *           +-inf is rejected.
  *   out_dtype : BASED_BF16 (round to nearest even) or BASED_F32.
  * Gets its workspace with hipMallocAsync / hipFreeAsync on `stream` (stream-ordered).
  */

@@ -8,8 +8,9 @@ Source: the page "Write a fast Based (Taylor linear attention) forward kernel" (
   * spec_md        - the definition: weights A[i,j] = 1 + s + s^2/2 for j <= i (else 0), s = scale*(q_i . k_j),
                      o_i = sum_j A[i,j] v_j / (sum_j A[i,j] + 1e-6); and the feature-map identity
                      phi(x) = [1, x, x (x) x / sqrt(2)], phi(q).phi(k) = 1 + (q.k) + (q.k)^2 / 2.
-  * contract_md    - scale=None means K**-0.5 (K, not V); scale multiplies q only; +1e-6 is added after the
-                     row sum; causal including the diagonal.
+  * contract_md    - the default scale is the inverse square root of the key width K; the scale is applied
+                     to the query side; the 1e-6 guard goes on after the row sum; the causal sum includes
+                     the diagonal.
   * reference_src  - the chunked feature-map algorithm: per chunk, read out with the state of earlier chunks
                      plus the direct polynomial inside the chunk, then fold the chunk into the state.
 
@@ -44,7 +45,8 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 def resolve_scale(scale, K: int) -> float:
-    """contract_md: None means K**-0.5 (the feature dimension K, not V). Rounded to float32 once."""
+    """contract_md: no scale given means the inverse square root of the key width K (V does not enter).
+    Rounded to float32 once."""
     if scale is None:
         scale = K ** -0.5
     return float(np.float32(scale))
@@ -141,7 +143,7 @@ def based_ref_chunked_state(q, k, v, scale=None, state=None, chunk: int = 256):
 
     reference_src starts from S = z = 0 and keeps S = sum_j phi(k_j) v_j^T (P x V) and z = sum_j phi(k_j)
     (length P) over the tokens already processed. Here `state` = (S0, z0) of shapes (B, H, P, V) and (B, H, P),
-    in the layout of `phi` (k unscaled: the scale multiplies q only, contract_md), stands for tokens that came
+    in the layout of `phi` (k unscaled, the scale being on the query side, contract_md), stands for tokens that came
     before this call; None means no earlier tokens. Returns (o, (S, z)) with the state after the last token.
     Processing a sequence in pieces, each starting from the state the previous piece returned, is the same
     computation as one call over the whole sequence."""
@@ -152,7 +154,7 @@ def based_ref_chunked_state(q, k, v, scale=None, state=None, chunk: int = 256):
     V = v.shape[-1]
     P = feature_dim(K)
     sigma = resolve_scale(scale, K)
-    qh = np.transpose(q, (0, 2, 1, 3)) * sigma      # (B, H, T, K), scale multiplies q only (contract_md)
+    qh = np.transpose(q, (0, 2, 1, 3)) * sigma      # (B, H, T, K), the scale on the query side (contract_md)
     kh = np.transpose(k, (0, 2, 1, 3))
     vh = np.transpose(v, (0, 2, 1, 3))
     if state is None:

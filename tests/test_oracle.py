@@ -186,7 +186,8 @@ def test_constant_values_give_constant_output():
 
 
 def test_default_scale_uses_K_not_V():
-    """contract_md: scale=None means K**-0.5 (note: K, not V)."""
+    """contract_md: with no scale given, the default is the inverse square root of the key width K; the
+    value width V plays no part (here K = 4, so the default equals an explicit 0.5)."""
     q, k, v = qkv(1, 50, 1, 4, 16, seed=12)
     d = based_ref_direct(q, k, v, None)
     np.testing.assert_allclose(d, based_ref_direct(q, k, v, 0.5), rtol=0, atol=0)
