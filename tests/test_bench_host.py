@@ -37,8 +37,22 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
-def test_traffic_figure_only_for_its_workload():
-    assert bench.measured_traffic("b2_t2048_h8_k16_v64") is None
+def test_traffic_figure_only_for_its_workload_and_code(monkeypatch):
+    """A traffic figure is read only from its own workload's summary, and only while the device code is the
+    one the counters were taken on."""
+    assert bench.measured_traffic("no_such_workload") is None
+    path = bench.traffic_file("b4_t8192_h16_k16_v64")
+    if not os.path.exists(path):
+        return
+    recorded = None
+    for line in open(path):
+        if line.strip().startswith("device_code_sha256:"):
+            recorded = line.split(":", 1)[1].strip()
+    assert recorded is not None
+    monkeypatch.setattr(bench, "device_code_digest", lambda lib=None: "0" * 64)
+    assert bench.measured_traffic("b4_t8192_h16_k16_v64") is None
+    monkeypatch.setattr(bench, "device_code_digest", lambda lib=None: recorded)
+    assert bench.measured_traffic("b4_t8192_h16_k16_v64") > bench.algorithmic_bytes(4, 8192, 16, 16, 64, 2)
 
 
 def test_oracle_baseline_leg():
