@@ -45,6 +45,7 @@ __host__ __device__ __forceinline__ void constexpr_for(F&& f) {
 // multiples of it) and wavefronts per work item for feature dimension K and `item_cols` columns.
 int item_columns(int64_t V);
 int state_slot_floats(int64_t K, int64_t item_cols);
+int state_value_groups(int64_t K, int64_t item_cols);
 int chunk_tokens(int64_t K, int64_t item_cols);
 int waves_per_item(int64_t K, int64_t item_cols);
 

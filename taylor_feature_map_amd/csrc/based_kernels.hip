@@ -476,16 +476,28 @@ __device__ __forceinline__ void load_value_operands(const Stage<Cf>& st, int ks,
   vop[Cf::ONES] = u32x4_t{kOnesBf16x2, kOnesBf16x2, kOnesBf16x2, kOnesBf16x2};
 }
 
-// Register-native layout of one segment state sum of a work item with VS value columns in the workspace,
-// 16 bytes (the four rows r) per lane and tile: the value tiles as [tile][value tile][lane][r], then the
-// ones tile, whose 16 columns are equal, as [tile][lane group][r].
-template <int VS>
+// Register-native layout of one segment state sum of a work item with VS value columns in the workspace:
+// the value tiles, 4 entries (the rows r) per lane and tile, as [tile][value tile][lane][r]; then the ones
+// tile (z, whose 16 columns are equal) in fp32, 16 bytes per lane group, as [tile][lane group][r]. The value
+// tiles are bf16 (8 bytes per lane and tile): the read-out rounds the state to bf16 for its products every
+// chunk anyway, so rounding a sum once more costs at most about one bf16 unit of it, while z keeps fp32 (its
+// constant feature counts the tokens, exactly in fp32 up to 2^24, and it divides every output). The K = 16,
+// 128-column read-out, at the edge of its registers, keeps fp32 value tiles (16 bytes). Offsets in bytes.
+template <int K, int VS>
+constexpr bool kBf16Slot = !(K == 16 && VS == 128);
+template <int K, int VS>
 __device__ __forceinline__ int64_t state_offset(int t, int vt, int lane) {
-  return ((t * (VS / 16) + vt) * kWave + lane) * 4;
+  return ((t * (VS / 16) + vt) * kWave + lane) * (kBf16Slot<K, VS> ? 8 : 16);
 }
 template <int K, int VS>
 __device__ __forceinline__ int64_t ones_offset(int t, int g) {
-  return Feat<K>::NPT * (VS / 16) * 4 * kWave + (t * 4 + g) * 4;
+  return Feat<K>::NPT * (VS / 16) * kWave * (kBf16Slot<K, VS> ? 8 : 16) + (t * 4 + g) * 16;
+}
+__device__ __forceinline__ u32x2_t to_bf16x4(const f32x4_t& x) {
+  return u32x2_t{pack2(x[0], x[1]), pack2(x[2], x[3])};
+}
+__device__ __forceinline__ f32x4_t from_bf16x4(const u32x2_t& u) {
+  return f32x4_t{lo_f(u.x), hi_f(u.x), lo_f(u.y), hi_f(u.y)};
 }
 
 struct ItemCoords {
@@ -628,7 +640,7 @@ struct __align__(16) StateSmem {
 // half: which 64 columns of the slot's IVS columns this work item covers (the ones tile goes with half 0).
 template <class SC, int IVS, int WI>
 __device__ __forceinline__ void segment_state_body(StateSmem<SC>& sm, const Rows& rw, int64_t T, int64_t t_begin,
-                                                   int64_t t_end, int half, float* __restrict__ dst) {
+                                                   int64_t t_end, int half, char* __restrict__ dst) {
   using SP = Split<SC>;
   using SS = StateSplit<SC>;
   constexpr int K = SC::K;
@@ -699,8 +711,13 @@ __device__ __forceinline__ void segment_state_body(StateSmem<SC>& sm, const Rows
 #pragma unroll
     for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-      for (int vt = 0; vt < SC::NVV; ++vt)
-        *reinterpret_cast<f32x4_t*>(dst + state_offset<IVS>(T0 + lt, SC::NVV * half + vt, lane)) = S[lt][vt];
+      for (int vt = 0; vt < SC::NVV; ++vt) {
+        char* d = dst + state_offset<K, IVS>(T0 + lt, SC::NVV * half + vt, lane);
+        if constexpr (kBf16Slot<K, IVS>)
+          *reinterpret_cast<u32x2_t*>(d) = to_bf16x4(S[lt][vt]);
+        else
+          *reinterpret_cast<f32x4_t*>(d) = S[lt][vt];
+      }
     if (half == 0 && c == 0) {
 #pragma unroll
       for (int lt = 0; lt < NT; ++lt)
@@ -724,7 +741,7 @@ __global__ __launch_bounds__((StateSplit<Cfg<K, 64>>::W * kWave), 2) void based_
   const int64_t t_end = t_begin + pl.seg_len;  // full segment: only the last one can be short
   const int64_t bhv = (ic.b * sh.H + ic.h) * pl.nvs + ic.vs / HALVES;
   const int half = static_cast<int>(ic.vs % HALVES);
-  float* dst = ws + (bhv * (pl.segments - 1) + ic.g) * pl.slot_floats;
+  char* dst = reinterpret_cast<char*>(ws + (bhv * (pl.segments - 1) + ic.g) * pl.slot_floats);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr_for<0, StateSplit<SC>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
@@ -735,38 +752,56 @@ __global__ __launch_bounds__((StateSplit<Cfg<K, 64>>::W * kWave), 2) void based_
 // ------------------------------------------------------------- kernel 1: prefix over segments
 
 // Used when there are too many segments for each read-out to add up its predecessors' sums: in place,
-// slot s of every (b, h, work item columns) becomes the sum of the segment sums 0..s. One thread per four
-// consecutive state entries (a slot holds a multiple of four floats, 16-byte aligned); slots are read in
-// batches ahead of the running sum so that the loads of a batch do not wait for the stores of the previous
-// one; with up to 32 slots every load is issued before the first add.
-__global__ __launch_bounds__(256) void based_segment_scan_kernel(float* __restrict__ ws, int64_t n_bhv,
-                                                                 int64_t slots, int64_t slot_floats) {
+// slot s of every (b, h, work item columns) becomes the sum of the segment sums 0..s. One thread per group
+// of four consecutive state entries: the first `bf16_groups` groups of a slot are bf16 value-tile entries (8
+// bytes), the rest fp32 ones-tile entries (16 bytes); the running sum is kept in fp32 and each prefix is
+// rounded once. Slots are read in batches ahead of the running sum so that the loads of a batch do not wait
+// for the stores of the previous one; with up to 32 slots every load is issued before the first add.
+constexpr int kScanThreads = 256;
+
+template <typename U, typename Load, typename Store>
+__device__ __forceinline__ void scan_slots(char* p, int64_t slot_bytes, int64_t slots, Load ld, Store st) {
   constexpr int kBatch = 16;
-  const int64_t quads = slot_floats / 4;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= n_bhv * quads) return;
-  const int64_t bhv = idx / quads;
-  const int64_t e = (idx - bhv * quads) * 4;
-  float* p = ws + bhv * slots * slot_floats + e;
-  auto at = [&](int64_t s) { return reinterpret_cast<f32x4_t*>(p + s * slot_floats); };
-  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t cur[kBatch];
+  auto at = [&](int64_t s) { return reinterpret_cast<U*>(p + s * slot_bytes); };
+  // The batches stay in their stored form until they are added, so that the next batch's loads are still
+  // in flight while this batch is summed and stored.
+  const U zero = {};
+  U cur[kBatch];
 #pragma unroll
-  for (int j = 0; j < kBatch; ++j) cur[j] = j < slots ? *at(j) : zero4;
-  f32x4_t run = zero4;
+  for (int j = 0; j < kBatch; ++j) cur[j] = j < slots ? *at(j) : zero;
+  f32x4_t run = {0.f, 0.f, 0.f, 0.f};
   for (int64_t s0 = 0; s0 < slots; s0 += kBatch) {
-    f32x4_t nxt[kBatch];
+    U nxt[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) nxt[j] = s0 + kBatch + j < slots ? *at(s0 + kBatch + j) : zero4;
+    for (int j = 0; j < kBatch; ++j) nxt[j] = s0 + kBatch + j < slots ? *at(s0 + kBatch + j) : zero;
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (s0 + j < slots) {
-        run += cur[j];
-        *at(s0 + j) = run;
+        run += ld(cur[j]);
+        *at(s0 + j) = st(run);
       }
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) cur[j] = nxt[j];
+  }
+}
+
+__global__ __launch_bounds__(kScanThreads) void based_segment_scan_kernel(float* __restrict__ ws, int64_t n_bhv,
+                                                                 int64_t slots, int64_t slot_floats,
+                                                                 int64_t bf16_groups) {
+  const int64_t groups = bf16_groups + (slot_floats - 2 * bf16_groups) / 4;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kScanThreads + threadIdx.x;
+  if (idx >= n_bhv * groups) return;
+  const int64_t bhv = idx / groups;
+  const int64_t e = idx - bhv * groups;
+  const int64_t slot_bytes = slot_floats * 4;
+  char* base = reinterpret_cast<char*>(ws + bhv * slots * slot_floats);
+  if (e < bf16_groups) {
+    scan_slots<u32x2_t>(base + e * 8, slot_bytes, slots, [](const u32x2_t& u) { return from_bf16x4(u); },
+                        [](const f32x4_t& x) { return to_bf16x4(x); });
+  } else {
+    scan_slots<f32x4_t>(base + bf16_groups * 8 + (e - bf16_groups) * 16, slot_bytes, slots,
+                        [](const f32x4_t& x) { return x; }, [](const f32x4_t& x) { return x; });
   }
 }
 
@@ -922,35 +957,75 @@ __device__ __forceinline__ void initial_state(SA& S, const float* __restrict__ s
   for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
     for (int vt = 0; vt < Cf::NVT; ++vt) S[lt][vt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // Two slots are loaded before either is added (the additions keep the segment order).
-  auto load = [&](f32x4_t (&x)[NT > 0 ? NT : 1][Cf::NVT], int64_t i) {
-    const float* s = src + i * slot_floats;
+  if constexpr (kBf16Slot<Cf::K, Cf::VS>) {
+    // Two slots are loaded before either is added (the additions keep the segment order); the value tiles
+    // stay packed bf16 until they are added.
+    struct Slot {
+      u32x2_t v[NT > 0 ? NT : 1][Cf::NVV];
+      f32x4_t z[NT > 0 ? NT : 1];
+    };
+    auto load = [&](Slot& x, int64_t i) {
+      const char* s = reinterpret_cast<const char*>(src + i * slot_floats);
 #pragma unroll
-    for (int lt = 0; lt < NT; ++lt) {
+      for (int lt = 0; lt < NT; ++lt) {
 #pragma unroll
-      for (int vt = 0; vt < Cf::NVV; ++vt)
-        x[lt][vt] = *reinterpret_cast<const f32x4_t*>(s + state_offset<Cf::VS>(T0 + lt, vt, lane));
-      x[lt][Cf::ONES] = *reinterpret_cast<const f32x4_t*>(s + ones_offset<Cf::K, Cf::VS>(T0 + lt, g));
+        for (int vt = 0; vt < Cf::NVV; ++vt)
+          x.v[lt][vt] = *reinterpret_cast<const u32x2_t*>(s + state_offset<Cf::K, Cf::VS>(T0 + lt, vt, lane));
+        x.z[lt] = *reinterpret_cast<const f32x4_t*>(s + ones_offset<Cf::K, Cf::VS>(T0 + lt, g));
+      }
+    };
+    auto add = [&](const Slot& x) {
+#pragma unroll
+      for (int lt = 0; lt < NT; ++lt) {
+#pragma unroll
+        for (int vt = 0; vt < Cf::NVV; ++vt) S[lt][vt] += from_bf16x4(x.v[lt][vt]);
+        S[lt][Cf::ONES] += x.z[lt];
+      }
+    };
+    int64_t i = 0;
+    for (; i + 1 < n_src; i += 2) {
+      Slot x0, x1;
+      load(x0, i);
+      load(x1, i + 1);
+      add(x0);
+      add(x1);
     }
-  };
-  auto add = [&](const f32x4_t (&x)[NT > 0 ? NT : 1][Cf::NVT]) {
+    if (i < n_src) {
+      Slot x0;
+      load(x0, i);
+      add(x0);
+    }
+  } else {
+    // fp32 slots; two are loaded before either is added (the additions keep the segment order).
+    auto load = [&](f32x4_t (&x)[NT > 0 ? NT : 1][Cf::NVT], int64_t i) {
+      const char* s = reinterpret_cast<const char*>(src + i * slot_floats);
 #pragma unroll
-    for (int lt = 0; lt < NT; ++lt)
+      for (int lt = 0; lt < NT; ++lt) {
 #pragma unroll
-      for (int vt = 0; vt < Cf::NVT; ++vt) S[lt][vt] += x[lt][vt];
-  };
-  int64_t i = 0;
-  for (; i + 1 < n_src; i += 2) {
-    f32x4_t x0[NT > 0 ? NT : 1][Cf::NVT], x1[NT > 0 ? NT : 1][Cf::NVT];
-    load(x0, i);
-    load(x1, i + 1);
-    add(x0);
-    add(x1);
-  }
-  if (i < n_src) {
-    f32x4_t x0[NT > 0 ? NT : 1][Cf::NVT];
-    load(x0, i);
-    add(x0);
+        for (int vt = 0; vt < Cf::NVV; ++vt)
+          x[lt][vt] = *reinterpret_cast<const f32x4_t*>(s + state_offset<Cf::K, Cf::VS>(T0 + lt, vt, lane));
+        x[lt][Cf::ONES] = *reinterpret_cast<const f32x4_t*>(s + ones_offset<Cf::K, Cf::VS>(T0 + lt, g));
+      }
+    };
+    auto add = [&](const f32x4_t (&x)[NT > 0 ? NT : 1][Cf::NVT]) {
+#pragma unroll
+      for (int lt = 0; lt < NT; ++lt)
+#pragma unroll
+        for (int vt = 0; vt < Cf::NVT; ++vt) S[lt][vt] += x[lt][vt];
+    };
+    int64_t i = 0;
+    for (; i + 1 < n_src; i += 2) {
+      f32x4_t x0[NT > 0 ? NT : 1][Cf::NVT], x1[NT > 0 ? NT : 1][Cf::NVT];
+      load(x0, i);
+      load(x1, i + 1);
+      add(x0);
+      add(x1);
+    }
+    if (i < n_src) {
+      f32x4_t x0[NT > 0 ? NT : 1][Cf::NVT];
+      load(x0, i);
+      add(x0);
+    }
   }
 }
 
@@ -1319,10 +1394,11 @@ hipError_t launch_segment_state(const void* k, const void* v, const Shape& sh, c
 
 hipError_t launch_segment_scan(const Shape& sh, const Plan& pl, float* ws, hipStream_t stream) {
   const int64_t n_bhv = sh.B * sh.H * pl.nvs;
-  const int64_t total = n_bhv * (pl.slot_floats / 4);
-  const int64_t blocks = (total + 255) / 256;
-  hipLaunchKernelGGL(based_segment_scan_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, ws,
-                     n_bhv, pl.segments - 1, pl.slot_floats);
+  const int64_t bf16_groups = state_value_groups(sh.K, pl.item_cols);
+  const int64_t total = n_bhv * (bf16_groups + (pl.slot_floats - 2 * bf16_groups) / 4);
+  const int64_t blocks = (total + kScanThreads - 1) / kScanThreads;
+  hipLaunchKernelGGL(based_segment_scan_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScanThreads), 0, stream, ws,
+                     n_bhv, pl.segments - 1, pl.slot_floats, bf16_groups);
   return hipGetLastError();
 }
 
@@ -1404,8 +1480,17 @@ hipError_t scratch_buffer(hipStream_t stream, void** ptr) {
 
 int item_columns(int64_t V) { return V % 128 == 0 ? 128 : 64; }
 
+// Groups of four bf16 value-tile entries in one segment sum (none where the slot keeps fp32 value tiles),
+// and its size in 4-byte words (the value tiles, then the ones tile in fp32: 16 words per feature tile).
+int state_value_groups(int64_t K, int64_t VS) {
+  if (K == 16 && VS == 128) return 0;  // fp32 value tiles (kBf16Slot)
+  return (K == 16 ? Feat<16>::NPT : Feat<8>::NPT) * static_cast<int>(VS / 16) * kWave;
+}
+
 int state_slot_floats(int64_t K, int64_t VS) {
-  return (K == 16 ? Feat<16>::NPT : Feat<8>::NPT) * (static_cast<int>(VS / 16) * 4 * kWave + 16);
+  const int npt = K == 16 ? Feat<16>::NPT : Feat<8>::NPT;
+  const int values = npt * static_cast<int>(VS / 16) * kWave * 4;  // value-tile entries
+  return (K == 16 && VS == 128 ? values : values / 2) + npt * 16;
 }
 
 int chunk_tokens(int64_t K, int64_t VS) {

@@ -10,9 +10,11 @@ from taylor_feature_map_amd import plan  # noqa: E402
 
 
 def slot_floats(K, cols):
-    # fp32 words of one segment sum: per feature tile, the value tiles' 64 lanes x 4 rows, plus the ones
-    # tile's 16 (10 tiles for K = 16, 3 for K = 8)
-    return (10 if K == 16 else 3) * ((cols // 16) * 4 * 64 + 16)
+    # 4-byte words of one segment sum: per feature tile, the value tiles' 64 lanes x 4 rows in bf16 (half a
+    # word each; fp32 for K = 16 with 128 columns), plus the ones tile's 16 in fp32 (10 tiles for K = 16, 3
+    # for K = 8)
+    per_entry = 1.0 if (K == 16 and cols == 128) else 0.5
+    return (10 if K == 16 else 3) * (int((cols // 16) * 4 * 64 * per_entry) + 16)
 
 
 def chunk(K, cols):
