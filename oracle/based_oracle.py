@@ -130,23 +130,40 @@ def feature_dim(K: int) -> int:
 
 
 def based_ref_chunked(q, k, v, scale=None, chunk: int = 256):
-    """reference_src, step for step: scale q; S = z = 0; for each chunk of `chunk` tokens:
-    num = phi(q_c) S + A v_c and den = phi(q_c) z + rowsum(A) with A the causal Taylor weights of the chunk,
-    o_c = num / (den + 1e-6); then S += phi(k_c)^T v_c and z += sum of phi(k_c) over the chunk.
-    All (b, h) pairs are processed together; every quantity is float64."""
+    """The chunked feature-map algorithm (reference_src) from empty sums, chunks of `chunk` tokens, every
+    quantity float64: `based_ref_chunked_state` with no earlier tokens."""
     o, _ = based_ref_chunked_state(q, k, v, scale, None, chunk)
     return o
 
 
-def based_ref_chunked_state(q, k, v, scale=None, state=None, chunk: int = 256):
-    """The algorithm of `based_ref_chunked` with its state carried across the call boundary.
+class _Carry:
+    """The running sums of one (b, h) pair over the tokens already seen (reference_src's state): S = sum of
+    phi(k_j) v_j^T (P x V) and z = sum of phi(k_j) (length P), in the layout of `phi`."""
 
-    reference_src starts from S = z = 0 and keeps S = sum_j phi(k_j) v_j^T (P x V) and z = sum_j phi(k_j)
-    (length P) over the tokens already processed. Here `state` = (S0, z0) of shapes (B, H, P, V) and (B, H, P),
-    in the layout of `phi` (k unscaled, the scale being on the query side, contract_md), stands for tokens that came
-    before this call; None means no earlier tokens. Returns (o, (S, z)) with the state after the last token.
-    Processing a sequence in pieces, each starting from the state the previous piece returned, is the same
-    computation as one call over the whole sequence."""
+    def __init__(self, S, z):
+        self.S = np.array(S, dtype=np.float64)
+        self.z = np.array(z, dtype=np.float64)
+
+    def read(self, feats):
+        """Numerator rows feats @ S and denominators feats @ z for feature rows `feats` (n x P)."""
+        return feats @ self.S, feats @ self.z
+
+    def fold(self, feats, values):
+        """Add tokens with feature rows `feats` (n x P) and value rows `values` (n x V)."""
+        self.S += feats.T @ values
+        self.z += feats.sum(axis=0)
+
+
+def based_ref_chunked_state(q, k, v, scale=None, state=None, chunk: int = 256):
+    """The chunked feature-map algorithm of reference_src with its state carried across the call boundary.
+
+    Each (b, h) pair is walked chunk by chunk. A chunk's outputs take the tokens before it through the
+    carried sums (phi of the scaled queries against S and z) and the tokens inside it directly through the
+    causal Taylor weights (diagonal included); then the chunk is folded into the sums. `state` = (S0, z0) of
+    shapes (B, H, P, V) and (B, H, P), in the layout of `phi` (k unscaled, the scale being on the query side,
+    contract_md), stands for tokens that came before this call; None means no earlier tokens. Returns
+    (o, (S, z)) with the sums after the last token, so a sequence processed in pieces, each starting from the
+    sums the previous piece returned, gives the same outputs as one call over the whole sequence."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -154,51 +171,51 @@ def based_ref_chunked_state(q, k, v, scale=None, state=None, chunk: int = 256):
     V = v.shape[-1]
     P = feature_dim(K)
     sigma = resolve_scale(scale, K)
-    qh = np.transpose(q, (0, 2, 1, 3)) * sigma      # (B, H, T, K), the scale on the query side (contract_md)
-    kh = np.transpose(k, (0, 2, 1, 3))
-    vh = np.transpose(v, (0, 2, 1, 3))
     if state is None:
-        S = np.zeros((B, H, P, V))                 # sum_j phi(k_j) v_j^T over earlier chunks
-        z = np.zeros((B, H, P))                    # sum_j phi(k_j) over earlier chunks
+        S0, z0 = np.zeros((B, H, P, V)), np.zeros((B, H, P))
     else:
-        S = np.array(state[0], dtype=np.float64).reshape(B, H, P, V)
-        z = np.array(state[1], dtype=np.float64).reshape(B, H, P)
-    tri = np.tri(chunk, chunk)
-    o = np.empty((B, H, T, V))
-    for i in range(0, T, chunk):
-        qc, kc, vc = qh[:, :, i:i + chunk], kh[:, :, i:i + chunk], vh[:, :, i:i + chunk]
-        n = qc.shape[2]
-        pq = phi(qc)                                               # (B, H, n, P)
-        s = qc @ np.swapaxes(kc, -1, -2)                           # (B, H, n, n)
-        A = taylor_weight(s) * tri[:n, :n]
-        num = pq @ S + A @ vc
-        den = np.einsum("bhnp,bhp->bhn", pq, z) + A.sum(-1)
-        o[:, :, i:i + n] = num / (den + DEN_GUARD)[..., None]
-        pk = phi(kc)
-        S = S + np.swapaxes(pk, -1, -2) @ vc
-        z = z + pk.sum(axis=2)
-    return np.ascontiguousarray(np.transpose(o, (0, 2, 1, 3))), (S, z)
+        S0 = np.asarray(state[0], dtype=np.float64).reshape(B, H, P, V)
+        z0 = np.asarray(state[1], dtype=np.float64).reshape(B, H, P)
+    o = np.empty((B, T, H, V))
+    S_end, z_end = np.empty((B, H, P, V)), np.empty((B, H, P))
+    for b in range(B):
+        for h in range(H):
+            carry = _Carry(S0[b, h], z0[b, h])
+            for lo in range(0, T, chunk):
+                hi = min(T, lo + chunk)
+                qs = sigma * q[b, lo:hi, h]                      # scaled queries of the chunk (contract_md)
+                kc, vc = k[b, lo:hi, h], v[b, lo:hi, h]
+                numer, denom = carry.read(phi(qs))               # the tokens before the chunk
+                w = np.tril(taylor_weight(qs @ kc.T))            # the chunk itself: row t sees keys j <= t
+                numer = numer + w @ vc
+                denom = denom + w.sum(axis=1)
+                o[b, lo:hi, h] = numer / (denom + DEN_GUARD)[:, None]
+                carry.fold(phi(kc), vc)
+            S_end[b, h], z_end[b, h] = carry.S, carry.z
+    return o, (S_end, z_end)
 
 
 def based_ref_decode_step(q1, k1, v1, state, scale=None):
     """One token of the same recurrence: q1, k1 of shape (B, H, K) and v1 of shape (B, H, V) are the next
-    token of every (b, h); state = (S, z) as in `based_ref_chunked_state`. The token is folded into the state
+    token of every (b, h); state = (S, z) as in `based_ref_chunked_state`. The token is folded into the sums
     first (the diagonal j = i is part of the causal sum, contract_md), then read out:
     o = phi(scale q) S' / (phi(scale q) z' + 1e-6). Returns (o of shape (B, H, V), (S', z'))."""
     q1 = np.asarray(q1, dtype=np.float64)
     k1 = np.asarray(k1, dtype=np.float64)
     v1 = np.asarray(v1, dtype=np.float64)
-    K = q1.shape[-1]
+    B, H, K = q1.shape
     sigma = resolve_scale(scale, K)
     S = np.array(state[0], dtype=np.float64)
     z = np.array(state[1], dtype=np.float64)
-    pk = phi(k1)                                                   # (B, H, P)
-    S = S + pk[..., :, None] * v1[..., None, :]
-    z = z + pk
-    pq = phi(sigma * q1)
-    num = np.einsum("bhp,bhpv->bhv", pq, S)
-    den = np.einsum("bhp,bhp->bh", pq, z)
-    return num / (den + DEN_GUARD)[..., None], (S, z)
+    o = np.empty(v1.shape)
+    for b in range(B):
+        for h in range(H):
+            carry = _Carry(S[b, h], z[b, h])
+            carry.fold(phi(k1[b, h])[None, :], v1[b, h][None, :])
+            numer, denom = carry.read(phi(sigma * q1[b, h])[None, :])
+            o[b, h] = numer[0] / (denom[0] + DEN_GUARD)
+            S[b, h], z[b, h] = carry.S, carry.z
+    return o, (S, z)
 
 
 # --------------------------------------------------------------------------------------------------------
