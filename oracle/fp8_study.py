@@ -45,16 +45,16 @@ def round_to_format(x, fmt: str):
     return np.clip(r, -fmax, fmax)
 
 
-def _blocks_scaled(x, fmt: str, axis: int):
-    """Round x with one power-of-two scale per block of 32 entries along `axis` (the contraction axis) and
-    per position of every other axis, so that each block's largest magnitude lands in the top binade."""
+def _blocks_scaled(x, fmt: str, axis: int, block: int = 32):
+    """Round x with one power-of-two scale per block of `block` entries along `axis` (the contraction axis)
+    and per position of every other axis, so that each block's largest magnitude lands in the top binade."""
     if fmt in ("f64", "bf16"):
         return round_to_format(x, fmt)
     x = np.moveaxis(np.asarray(x, dtype=np.float64), axis, -1)
     n = x.shape[-1]
-    pad = (-n) % 32
+    pad = (-n) % block
     xp = np.concatenate([x, np.zeros(x.shape[:-1] + (pad,))], axis=-1) if pad else x
-    xb = xp.reshape(xp.shape[:-1] + (-1, 32))
+    xb = xp.reshape(xp.shape[:-1] + (-1, block))
     amax = np.max(np.abs(xb), axis=-1, keepdims=True)
     fmax = FORMATS[fmt][2]
     scale = np.exp2(np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - np.floor(np.log2(fmax)))
@@ -63,9 +63,30 @@ def _blocks_scaled(x, fmt: str, axis: int):
     return np.moveaxis(y, -1, axis)
 
 
-def emulate_forward(q, k, v, scale=None, chunk: int = 128, intra="bf16", readout="bf16", update="bf16"):
+def _features_rounded(f, fmt: str, feat_axis: int, contract_axis: int, block: int, K: int, quad_only: bool):
+    """phi features (along feat_axis) rounded as a product operand with scale blocks along contract_axis;
+    with quad_only the constant and linear features (the first 1 + K, whose range differs from the
+    quadratic block's) stay bf16."""
+    if not quad_only:
+        return _blocks_scaled(f, fmt, contract_axis, block)
+    f = np.asarray(f, dtype=np.float64)
+    n = f.ndim
+    fa = feat_axis % n
+    ca = contract_axis % n
+    idx = [slice(None)] * n
+    idx[fa] = slice(0, 1 + K)
+    head = round_to_format(f[tuple(idx)], "bf16")
+    idx[fa] = slice(1 + K, None)
+    quad = _blocks_scaled(f[tuple(idx)], fmt, ca, block)
+    return np.concatenate([head, quad], axis=fa)
+
+
+def emulate_forward(q, k, v, scale=None, chunk: int = 128, intra="bf16", readout="bf16", update="bf16",
+                    block: int = 32, quad_only: bool = False):
     """The chunked algorithm with rounded operands (see the module text). Inputs as for the oracle routes:
-    float arrays holding bf16 values, q, k (B, T, H, K), v (B, T, H, V). Returns o (B, T, H, V) float64."""
+    float arrays holding bf16 values, q, k (B, T, H, K), v (B, T, H, V). `block` is the number of
+    contraction entries per scale; with quad_only only the quadratic feature block of phi(q) and phi(k) (and
+    the matching rows of S) take the read-out's and update's format. Returns o (B, T, H, V) float64."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -84,21 +105,21 @@ def emulate_forward(q, k, v, scale=None, chunk: int = 128, intra="bf16", readout
         qc, kc, vc = qh[:, :, i:i + chunk], kh[:, :, i:i + chunk], vh[:, :, i:i + chunk]
         n = qc.shape[2]
         # read-out of earlier chunks: phi(q) against [S | z], contraction over the P features
-        pq = _blocks_scaled(phi(qc), readout, axis=-1)
-        Sq = _blocks_scaled(S, readout, axis=-2)
-        zq = _blocks_scaled(z, readout, axis=-1)
+        pq = _features_rounded(phi(qc), readout, -1, -1, block, K, quad_only)
+        Sq = _features_rounded(S, readout, -2, -2, block, K, quad_only)
+        zq = _features_rounded(z, readout, -1, -1, block, K, quad_only)
         num = pq @ Sq
         den = np.einsum("bhnp,bhp->bhn", pq, zq)
         # inside the chunk: the Taylor weights against [v | 1], contraction over the keys
         A = taylor_weight(qc @ np.swapaxes(kc, -1, -2)) * tri[:n, :n]
-        Aq = _blocks_scaled(A, intra, axis=-1)
-        vq = _blocks_scaled(vc, intra, axis=-2)
+        Aq = _blocks_scaled(A, intra, axis=-1, block=block)
+        vq = _blocks_scaled(vc, intra, axis=-2, block=block)
         num = num + Aq @ vq
         den = den + Aq.sum(-1)
         o[:, :, i:i + n] = num / (den + DEN_GUARD)[..., None]
         # fold the chunk into the state: phi(k)^T [v | 1], contraction over the chunk's tokens
-        pk = _blocks_scaled(phi(kc), update, axis=-2)
-        vu = _blocks_scaled(vc, update, axis=-2)
+        pk = _features_rounded(phi(kc), update, -1, -2, block, K, quad_only)
+        vu = _blocks_scaled(vc, update, axis=-2, block=block)
         S = S + np.swapaxes(pk, -1, -2) @ vu
         z = z + pk.sum(axis=2)
     return np.ascontiguousarray(np.transpose(o, (0, 2, 1, 3)))
@@ -111,6 +132,11 @@ VARIANTS = (
     ("e4m3 update only", dict(intra="bf16", readout="bf16", update="e4m3")),
     ("e4m3 everywhere", dict(intra="e4m3", readout="e4m3", update="e4m3")),
     ("e5m2 everywhere", dict(intra="e5m2", readout="e5m2", update="e5m2")),
+    # narrower ranges: one scale per 8 contraction entries, or fp8 only for the quadratic feature block
+    ("e4m3 intra only, 8-entry scales", dict(intra="e4m3", readout="bf16", update="bf16", block=8)),
+    ("e4m3 read-out only, 8-entry scales", dict(intra="bf16", readout="e4m3", update="bf16", block=8)),
+    ("e4m3 read-out, quadratic features only", dict(intra="bf16", readout="e4m3", update="bf16", quad_only=True)),
+    ("e4m3 update, quadratic features only", dict(intra="bf16", readout="bf16", update="e4m3", quad_only=True)),
 )
 
 
