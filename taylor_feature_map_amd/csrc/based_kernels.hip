@@ -621,7 +621,7 @@ struct StateSplit {
   static constexpr int W = FW * KW;
   __host__ __device__ static constexpr int T0(int fg) { return K16 ? (fg < 2 ? 3 * fg : 6 + 2 * (fg - 2)) : 0; }
   __host__ __device__ static constexpr int NT(int fg) { return K16 ? (fg < 2 ? 3 : 2) : 3; }
-  static constexpr int NT_MAX = K16 ? 3 : 3;
+  static constexpr int NT_MAX = 3;  // the largest feature group (both splits)
   static constexpr int KS = Split<Cf>::NKS / KW;  // key steps per wave and chunk
   // Chunks loaded ahead of the one being worked on: with K = 8 there is less work per chunk to cover the
   // latency of the loads (measured: 3 sets are 18% faster than 1 at K = 8, V = 128; no change at K = 16).
@@ -905,11 +905,12 @@ __device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t ro, unsigned v
 // chunk at the end of the iteration: wave WI's prefetch units WI * 64 + i * 64 W .. + 63 occupy bytes
 // 1024 (WI + W i) .. + 1023 of a stage, and no wave reads that stage before the next barrier, so no barrier
 // is needed (a wave's own LDS accesses are carried out in order). A block holds RB = 1024 / (2 VS) rows of
-// the tile in plain row order, so that every address is one lane base plus a constant (a swizzle against
-// the bank conflicts of the 8-byte writes would cost a live address register per value tile, more than
-// the conflicts cost). Later, once the registers of the chunk's contraction are free, the rows are read
-// back as UPR 16-byte units each and stored with one 128-bit store per lane, so every store instruction
-// covers RB whole rows of the output (32 bytes of each of 16 rows in the register layout otherwise).
+// the tile; the 16-byte unit u of tile row r sits at unit position u ^ (r % UPR), which spreads the 8-byte
+// writes of one value tile over all banks (in plain row order they fell on a quarter of them, and the
+// read-out was 20% slower). Later, once the registers of the chunk's contraction are free, the rows are
+// read back as UPR 16-byte units each and stored with one 128-bit store per lane, so every store
+// instruction covers RB whole rows of the output (32 bytes of each of 16 rows in the register layout
+// otherwise).
 template <class Cf, int WI, int II>
 struct TileRows {
   static constexpr int W = Split<Cf>::W;
