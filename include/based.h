@@ -174,9 +174,11 @@ based_status_t based_decode_step(const void* q, const void* k, const void* v,
 /* The sequence is split into `segments` pieces of `segment_len` tokens (the last may be shorter); each
  * piece of each (b, h, group of 64 value columns, or 128 when V is a multiple of 128) is processed by one
  * workgroup in chunks of 64 tokens (128 for 128 columns with K = 16); a first kernel sums the state of
- * every piece but the last into the workspace, and the read-out of piece g starts from the sum of the
- * sums of pieces 0 .. g - 1 (with more than 16 pieces, a prefix-scan kernel forms those sums in between).
- * Reports the plan chosen for a shape; segment_len_override > 0 forces that length (rounded up to a
+ * every piece but the last into the workspace (each in two halves when it would otherwise run at most one
+ * workgroup per compute unit and the halves are at least 1024 tokens), and the read-out of piece g starts
+ * from the sum of those sums for pieces 0 .. g - 1 (with more than 15 such sums before a piece, a
+ * prefix-scan kernel forms the running sums in between). Reports the plan chosen for a shape (the
+ * workspace size tells the number of sums); segment_len_override > 0 forces that length (rounded up to a
  * whole number of chunks). */
 based_status_t based_forward_plan(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
                                   int64_t segment_len_override, int64_t* segments,

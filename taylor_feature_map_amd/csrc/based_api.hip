@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -37,6 +38,8 @@ constexpr int64_t kTargetWaves = 2048;           // 256 CUs x 4 SIMDs x 2 reside
 // of the earlier segments' sums (or a scan kernel) cost more than the shorter chains gain.
 constexpr int64_t kShortSegment = 256;
 constexpr int64_t kMaxShortSegments = 8;
+// Shortest piece of a segment the state pass sums on its own (see make_plan).
+constexpr int64_t kMinPiece = 1024;
 constexpr int64_t kMaxRowRange = 0x7fffffff;     // bytes addressable through one 32-bit buffer range
 
 based_status_t check_shape(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V) {
@@ -107,7 +110,16 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
   pl.seg_len = L;
   pl.segments = (sh.T + L - 1) / L;
   pl.slot_floats = based::state_slot_floats(sh.K, pl.item_cols);
-  pl.scanned = pl.segments > based::kMaxSummedSegments;
+  // The state pass sums each segment but the last in sub pieces. Two pieces when one per segment would give
+  // it at most one workgroup per CU and the halves stay long (kMinPiece tokens, whole 64-token chunks): a
+  // state workgroup runs its chunks about as fast with a second one on its CU as alone, so the pass takes
+  // about half the time, while each read-out adds up twice as many sums.
+  pl.sub = 1;
+  if (pl.segments > 1) {
+    const int64_t state_items = sh.B * sh.H * pl.nvs * (pl.item_cols / 64) * (pl.segments - 1);
+    if (state_items <= kCUs && pl.seg_len % 128 == 0 && pl.seg_len / 2 >= kMinPiece) pl.sub = 2;
+  }
+  pl.scanned = based::state_slots(pl) > based::kMaxSummedSlots;
   // XCD-affine items when the (b, columns, h) pairs split evenly over the 8 XCDs and each XCD's run of
   // heads covers whole 128-byte lines of the q and k rows (64 / K heads per line).
   const int64_t pairs = sh.B * sh.H * pl.nvs, ppx = pairs / 8, line_heads = 64 / sh.K;
@@ -120,18 +132,19 @@ Plan make_plan(const Shape& sh, int64_t seg_override) {
   return pl;
 }
 
-// The kernels number their work items in 32 bits: (b, h, columns, segment) for the read-out, twice as many
-// 64-column halves per segment (but one segment fewer) for the state sums.
+// The kernels number their work items in 32 bits: (b, h, columns, segment) for the read-out, up to two
+// 64-column halves per state sum for the state pass.
 based_status_t check_items(const Shape& sh, const Plan& pl) {
   const int64_t pairs = sh.B * sh.H * pl.nvs;
-  if (pairs > based::kMaxItems / pl.segments / 2)
+  const int64_t per_pair = 2 * std::max(pl.segments, based::state_slots(pl));
+  if (pairs > based::kMaxItems / per_pair)
     return fail(BASED_ERR_UNSUPPORTED, "too many work items: B * H * (V / columns) * segments must stay below 2^30");
   return BASED_OK;
 }
 
 size_t workspace_bytes(const Shape& sh, const Plan& pl) {
   if (pl.segments <= 1) return 0;
-  return static_cast<size_t>(sh.B * sh.H * pl.nvs * (pl.segments - 1) * pl.slot_floats) * sizeof(float);
+  return static_cast<size_t>(sh.B * sh.H * pl.nvs * based::state_slots(pl) * pl.slot_floats) * sizeof(float);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {

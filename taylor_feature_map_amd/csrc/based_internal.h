@@ -21,17 +21,21 @@ struct Shape {
 // predecessors itself.
 struct Plan {
   int64_t segments, seg_len, nvs, item_cols, slot_floats;
+  int64_t sub;  // state sums per segment: the state pass splits each segment but the last into sub pieces
   bool scanned;
   bool affine;  // XCD-affine work items (every segment of a (b, h, columns) pair on one XCD)
   bool row_stores;  // bf16 output tiles staged through LDS and stored as whole rows
 };
 
+// State sums per (b, h, item columns): sub for every segment but the last.
+__host__ __device__ __forceinline__ int64_t state_slots(const Plan& pl) { return (pl.segments - 1) * pl.sub; }
+
 // Upper bound on the work items (blocks) of one launch; below it all item index arithmetic fits in 32 bits.
 constexpr int64_t kMaxItems = (int64_t(1) << 31) - 8;
 
-// Most segments for which each read-out adds up its predecessors' sums itself (beyond this, the
-// quadratic number of slot reads costs more than a scan kernel).
-constexpr int64_t kMaxSummedSegments = 16;
+// Most state sums before a read-out's segment for which it adds them up itself (beyond this, the quadratic
+// number of slot reads costs more than a scan kernel).
+constexpr int64_t kMaxSummedSlots = 15;
 
 template <int B, int E, typename F>
 __host__ __device__ __forceinline__ void constexpr_for(F&& f) {

@@ -565,12 +565,12 @@ __device__ __forceinline__ bool readout_item(const Shape& sh, const Plan& pl, It
   return true;
 }
 
-// State item of this block (64-column halves: pair p of the read-out is halves p * HALVES ..); false for
-// padding blocks.
+// State item of this block (64-column halves: pair p of the read-out is halves p * HALVES ..; ic.g numbers
+// the pieces of pl.seg_len / pl.sub tokens); false for padding blocks.
 template <int HALVES>
 __device__ __forceinline__ bool state_item(const Shape& sh, const Plan& pl, ItemCoords& ic) {
   const uint32_t H = static_cast<uint32_t>(sh.H), NVS = static_cast<uint32_t>(pl.nvs);
-  const uint32_t G1 = static_cast<uint32_t>(pl.segments - 1);
+  const uint32_t G1 = static_cast<uint32_t>(state_slots(pl));
   const uint32_t pairs = static_cast<uint32_t>(sh.B) * H * NVS;
   if (pl.affine) {  // the grid is exactly pairs * HALVES * G1 blocks
     const uint32_t x = blockIdx.x, ppx = (pairs >> 3) * HALVES, j = x >> 3;
@@ -737,11 +737,12 @@ __global__ __launch_bounds__((StateSplit<Cfg<K, 64>>::W * kWave), 2) void based_
   if (!state_item<HALVES>(sh, pl, ic)) return;
   __shared__ StateSmem<SC> sm;
   const Rows rw = make_rows<K, 64>(k, k, v, sh, ic);
-  const int64_t t_begin = ic.g * pl.seg_len;
-  const int64_t t_end = t_begin + pl.seg_len;  // full segment: only the last one can be short
+  const int64_t len = pl.seg_len / pl.sub;
+  const int64_t t_begin = ic.g * len;
+  const int64_t t_end = t_begin + len;  // a whole piece: only the last segment, which has none, can be short
   const int64_t bhv = (ic.b * sh.H + ic.h) * pl.nvs + ic.vs / HALVES;
   const int half = static_cast<int>(ic.vs % HALVES);
-  char* dst = reinterpret_cast<char*>(ws + (bhv * (pl.segments - 1) + ic.g) * pl.slot_floats);
+  char* dst = reinterpret_cast<char*>(ws + (bhv * state_slots(pl) + ic.g) * pl.slot_floats);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr_for<0, StateSplit<SC>::W>([&](auto wc) {
     constexpr int WI = decltype(wc)::value;
@@ -1249,13 +1250,13 @@ __global__ __launch_bounds__((Split<Cfg<K, VS>>::W * kWave)) void based_chunk_re
       make_rsrc(static_cast<char*>(out) + bh_v * (OUT_F32 ? 4 : 2), sh.T, out_stride);
   const int64_t t_begin = ic.g * pl.seg_len;
   const int64_t t_end = (t_begin + pl.seg_len < sh.T) ? t_begin + pl.seg_len : sh.T;
-  // Initial state: the sum of the state sums of segments 0 .. g - 1, or after the prefix scan the single
-  // slot g - 1 that already holds it.
+  // Initial state: the sum of the state sums of the pieces of segments 0 .. g - 1 (g * sub of them), or after
+  // the prefix scan the single slot g * sub - 1 that already holds it.
   const int64_t bhv = (ic.b * sh.H + ic.h) * pl.nvs + ic.vs;
-  const float* src = ws + bhv * (pl.segments - 1) * pl.slot_floats;
-  int64_t n_src = ic.g;
+  const float* src = ws + bhv * state_slots(pl) * pl.slot_floats;
+  int64_t n_src = ic.g * pl.sub;
   if (pl.scanned && ic.g > 0) {
-    src += (ic.g - 1) * pl.slot_floats;
+    src += (ic.g * pl.sub - 1) * pl.slot_floats;
     n_src = 1;
   }
   StateView sv;
@@ -1401,7 +1402,7 @@ __global__ __launch_bounds__(NT) void based_decode_step_kernel(const u16* __rest
 template <int K, int VS>
 hipError_t launch_segment_state(const void* k, const void* v, const Shape& sh, const Plan& pl, float* ws,
                                 hipStream_t stream) {
-  const int64_t items = sh.B * sh.H * (pl.nvs * VS / 64) * (pl.segments - 1);
+  const int64_t items = sh.B * sh.H * (pl.nvs * VS / 64) * state_slots(pl);
   const int64_t blocks = (items + 7) / 8 * 8;
   hipLaunchKernelGGL((based_segment_state_kernel<K, VS>), dim3(static_cast<unsigned>(blocks)),
                      dim3(StateSplit<Cfg<K, 64>>::W * kWave), 0, stream, static_cast<const u16*>(k),
@@ -1415,7 +1416,7 @@ hipError_t launch_segment_scan(const Shape& sh, const Plan& pl, float* ws, hipSt
   const int64_t total = n_bhv * (bf16_groups + (pl.slot_floats - 2 * bf16_groups) / 4);
   const int64_t blocks = (total + kScanThreads - 1) / kScanThreads;
   hipLaunchKernelGGL(based_segment_scan_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kScanThreads), 0, stream, ws,
-                     n_bhv, pl.segments - 1, pl.slot_floats, bf16_groups);
+                     n_bhv, state_slots(pl), pl.slot_floats, bf16_groups);
   return hipGetLastError();
 }
 

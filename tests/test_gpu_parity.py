@@ -94,6 +94,32 @@ def test_parity_scanned_segments(K, V, seg):
     _gate(o, ref, f"K{K} V{V} seg{seg} G{g}")
 
 
+def _slot_floats(K, cols):
+    # 4-byte words of one state sum (value tiles bf16, fp32 for K = 16 with 128 columns; ones tile fp32)
+    per_entry = 1.0 if (K == 16 and cols == 128) else 0.5
+    return (10 if K == 16 else 3) * (int((cols // 16) * 4 * 64 * per_entry) + 16)
+
+
+@pytest.mark.parametrize("B,T,H,K,V,seg,scanned", [
+    (1, 4500, 2, 16, 64, 2048, False),   # three segments, the last ragged: four state sums
+    (1, 4500, 2, 8, 128, 2048, False),
+    (1, 4500, 2, 16, 128, 2048, False),  # 128-column items: both 64-column halves of each piece
+    (1, 18500, 1, 16, 64, 2048, True),   # ten segments, eighteen state sums: through the scan kernel
+])
+def test_parity_split_state_pieces(B, T, H, K, V, seg, scanned):
+    """Few state workgroups and long segments: the state pass sums each segment but the last in two pieces,
+    and each read-out adds up (or, scanned, reads the prefix of) twice as many sums."""
+    from taylor_feature_map_amd import plan
+    g, _, ws = plan(B, T, H, K, V, seg)
+    cols = 128 if V % 128 == 0 else 64
+    assert ws == B * H * (V // cols) * (g - 1) * 2 * _slot_floats(K, cols) * 4, "two pieces per segment"
+    assert ((g - 1) * 2 > 15) == scanned
+    qb, kb, vb = make_qkv(B, T, H, K, V, seed=31 + K + V)
+    ref = based_ref_chunked(bf16_to_f64(qb), bf16_to_f64(kb), bf16_to_f64(vb), None, 64)
+    o = _run(qb, kb, vb, None, torch.bfloat16, segment_len=seg)
+    _gate(o, ref, f"B{B} T{T} H{H} K{K} V{V} seg{seg} G{g}")
+
+
 @pytest.mark.parametrize("B,T,H,K,V", [(1, 1024, 4, 16, 64), (2, 1000, 4, 8, 128)])
 def test_parity_paired_segment_order(B, T, H, K, V):
     """Grids whose read-out blocks take the segments in the paired order (segment g beside G-1-g)."""

@@ -1,6 +1,7 @@
 """CPU checks of the work plan (`based_forward_plan`, host code, no GPU): for any shape the segments are
 whole chunks that cover the sequence exactly, segments shorter than 256 tokens come at most eight at a time,
-and the shapes whose plans were chosen by measurement keep them."""
+the state pass splits segments in two exactly where its rule says, and the shapes whose plans were chosen by
+measurement keep them."""
 import pytest
 
 hypothesis = pytest.importorskip("hypothesis")
@@ -32,14 +33,38 @@ def test_plan_invariants(B, T, H, K, V):
     assert G <= 8 or L >= 256, "more than eight segments shorter than 256 tokens"
     assert (ws == 0) == (G == 1)
     if G > 1:
-        # the workspace holds one sum per (b, h, item, segment but the last): it tells the item width
-        widths = [c for c in ((128, 64) if V % 128 == 0 else (64,))
-                  if ws == B * H * (V // c) * (G - 1) * slot_floats(K, c) * 4]
-        assert len(widths) == 1, (ws, widths)
-        C = chunk(K, widths[0])
+        # the workspace holds `sub` sums per (b, h, item, segment but the last): it tells the item width and
+        # the number of pieces the state pass sums each segment in
+        found = [(c, sub) for c in ((128, 64) if V % 128 == 0 else (64,)) for sub in (1, 2)
+                 if ws == B * H * (V // c) * (G - 1) * sub * slot_floats(K, c) * 4]
+        assert len(found) == 1, (ws, found)
+        width, sub = found[0]
+        C = chunk(K, width)
         assert L % C == 0 and L >= (2 if K == 16 else 1) * C
         if K == 8 or V % 128 != 0:
-            assert widths[0] == (128 if V % 128 == 0 else 64)
+            assert width == (128 if V % 128 == 0 else 64)
+        assert sub == (2 if split_pieces(B, H, V, width, G, L) else 1)
+
+
+def split_pieces(B, H, V, width, G, L):
+    # two pieces per segment when the state pass would have at most one workgroup per CU (256) and the
+    # pieces stay whole 64-token chunks of at least 1024 tokens
+    state_items = B * H * (V // width) * (width // 64) * (G - 1)
+    return state_items <= 256 and L % 128 == 0 and L // 2 >= 1024
+
+
+@pytest.mark.parametrize("shape,seg,sub", [
+    ((4, 16384, 32, 8, 128), 0, 2),      # 128 (b, h) pairs x 2 halves x 1 segment: two pieces (5% faster)
+    ((4, 8192, 16, 16, 64), 0, 1),       # 448 state workgroups already
+    ((8, 4096, 16, 16, 128), 2048, 2),   # forced two segments of 128-column items: 256 state workgroups
+    ((8, 4096, 16, 16, 128), 1024, 1),   # pieces of 512 tokens: too short
+    ((1, 65000, 16, 16, 64), 0, 1),
+])
+def test_state_pieces(shape, seg, sub):
+    B, T, H, K, V = shape
+    G, L, ws = plan(*shape, seg)
+    width = 128 if (V % 128 == 0 and ws == B * H * (V // 128) * (G - 1) * sub * slot_floats(K, 128) * 4) else 64
+    assert ws == B * H * (V // width) * (G - 1) * sub * slot_floats(K, width) * 4, (G, L, ws)
 
 
 @pytest.mark.parametrize("shape,G,L", [
