@@ -32,9 +32,10 @@
 //    swizzled against bank conflicts); V and K with the token index along the contraction come from
 //    ds_read_b64_tr_b16 transpose reads.
 //  * Long sequences are split into segments so that all SIMDs have work (two waves per SIMD): a first
-//    kernel sums phi(k)^T v per segment (every segment but the last), and the read-out of segment g
-//    starts from the sum of the sums of segments 0 .. g - 1, added in segment order at its start. With
-//    more than 16 segments a prefix-scan kernel turns the sums into those starting states first.
+//    kernel sums phi(k)^T v per segment (every segment but the last; per half segment when one workgroup
+//    per segment would leave it at most one per CU), and the read-out of segment g starts from the sum of
+//    the sums before it, added in sequence order at its start. With more than 15 such sums a prefix-scan
+//    kernel turns them into those starting states first.
 //  * Work items are placed on the 8 XCDs so that shared q/k cache lines, and where the heads allow it all
 //    segments of a (b, h) and hence the segment sums, stay in one XCD's L2 (readout_item, state_item).
 //  * The one-token decode step is a separate, purely memory-bound kernel over the state in the page's
@@ -752,8 +753,8 @@ __global__ __launch_bounds__((StateSplit<Cfg<K, 64>>::W * kWave), 2) void based_
 
 // ------------------------------------------------------------- kernel 1: prefix over segments
 
-// Used when there are too many segments for each read-out to add up its predecessors' sums: in place,
-// slot s of every (b, h, work item columns) becomes the sum of the segment sums 0..s. One thread per group
+// Used when there are too many state sums for each read-out to add up its predecessors' sums: in place,
+// slot s of every (b, h, work item columns) becomes the sum of the state sums 0..s. One thread per group
 // of four consecutive state entries: the first `bf16_groups` groups of a slot are bf16 value-tile entries (8
 // bytes), the rest fp32 ones-tile entries (16 bytes); the running sum is kept in fp32 and each prefix is
 // rounded once. Slots are read in batches ahead of the running sum so that the loads of a batch do not wait

@@ -83,7 +83,7 @@ def test_parity_forced_segments(K, V, seg):
 
 @pytest.mark.parametrize("K,V,seg", [(16, 64, 128), (8, 128, 64), (16, 128, 128)])
 def test_parity_scanned_segments(K, V, seg):
-    """More than 16 segments: the segment sums go through the prefix-scan kernel first."""
+    """More than 16 segments (more than 15 state sums): the sums go through the prefix-scan kernel first."""
     from taylor_feature_map_amd import plan
     B, T, H = 1, 2500, 2
     g, _, _ = plan(B, T, H, K, V, seg)
