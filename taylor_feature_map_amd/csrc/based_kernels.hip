@@ -1447,8 +1447,6 @@ hipError_t launch_chunk_readout(const void* q, const void* k, const void* v, con
   return hipGetLastError();
 }
 
-// Eight waves per (b, h): measured against four and sixteen over B x H from 64 to 8192 pairs, it is the
-// fastest or within 6% of it everywhere.
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, int64_t B, int64_t H, int64_t K,
                               int64_t V, float sigma, float* S, float* z, void* out, bool out_f32, hipStream_t stream) {
   // 512 threads for K = 16 (273 state rows), 256 for K = 8 (73 rows): measured 19% faster than 512 at
