@@ -85,6 +85,30 @@ def test_split_and_carry(K, V, T, cuts):
     _state_gate((_np(state[0]), _np(state[1])), st_ref, f"carried state K{K} V{V} T{T}")
 
 
+def test_state_in_and_out_with_split_state_pass():
+    """An automatic plan whose state pass sums each segment in two pieces (K = 8, V = 128, 128 heads,
+    T = 4096: two segments of 2048 tokens, 256 state workgroups) with a state carried in and out; outputs
+    and final states of six heads against the oracle started from the same state."""
+    from taylor_feature_map_amd import based_forward, plan
+    B, T, H, K, V = 1, 4096, 128, 8, 128
+    G, L, ws = plan(B, T, H, K, V)
+    slot_bytes = 3 * ((V // 16) * 4 * 64 // 2 + 16) * 4
+    assert (G, L) == (2, 2048) and ws == B * H * (G - 1) * 2 * slot_bytes, "two pieces per segment"
+    T0 = 300
+    qb, kb, vb = make_qkv(B, T0 + T, H, K, V, seed=4242)
+    q, k, v = bf16_to_f64(qb), bf16_to_f64(kb), bf16_to_f64(vb)
+    _, st0 = based_ref_chunked_state(q[:, :T0], k[:, :T0], v[:, :T0], None, None)
+    o, (S, z) = based_forward(_to_dev(qb[:, T0:]), _to_dev(kb[:, T0:]), _to_dev(vb[:, T0:]),
+                              initial_state=(_f32(st0[0]), _f32(st0[1])), return_state=True,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    heads = [0, 1, 37, 64, 101, 127]
+    o_ref, st_ref = based_ref_chunked_state(q[:, T0:, heads], k[:, T0:, heads], v[:, T0:, heads], None,
+                                            (st0[0][:, heads], st0[1][:, heads]))
+    _gate(_np(o)[:, :, heads], o_ref, "split state pass, state in and out")
+    _state_gate((_np(S)[:, heads], _np(z)[:, heads]), st_ref, "split state pass, final state")
+
+
 @pytest.mark.parametrize("K,V", [(16, 64), (8, 64)])
 def test_initial_state_only_symmetric_part_counts(K, V):
     """An antisymmetric matrix added to the quadratic block of the initial state changes no output."""
